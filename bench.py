@@ -1,0 +1,447 @@
+#!/usr/bin/env python3
+"""RMSNorm forward + backward throughput on one MI355X.
+
+A step is one pass of the hot path over one batch: forward (y, rstd) then the
+backward (dx and the dw partials, then the dw reduce pass) of the bf16
+4096 x 4096 workload (rows = B*T = 4096, H = 4096, outlier feature columns),
+through the library's C ABI.  Inputs are resident in HBM before timing.
+Buffer sets rotate so that consecutive steps touch >= 1 GiB of distinct
+memory, which keeps every step's inputs out of the 256 MB Infinity Cache.
+
+Prints one JSON line.  `value` is achieved HBM GB/s over the whole step,
+counting the algorithmic bytes only (fwd: x, w read, y, rstd written; bwd: dy,
+x, w, rstd read, dx, dw written).  `roofline` is for the dominant kernel (the
+backward row pass), timed with HIP events on the stream it runs on.
+`cpu_baseline` times the double-precision oracle on the host.
+
+--suite FILE also measures every workload (fwd, bwd, residual, narrow, wide,
+decode split-row) and writes one JSON object per measurement to FILE.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of MI355X peak) + µs/call, RMSNorm fwd and bwd"
+PEAK_GBS = 8000.0          # MI355X HBM3E
+COLD_BYTES = 1 << 30       # distinct memory touched by consecutive steps
+
+
+# ---------------------------------------------------------------- algorithmic bytes
+
+def fwd_bytes(rows, H, e, residual=False):
+    """x (+res) read, y (+h) written, rstd written, w read once."""
+    per_row = (4 if residual else 2) * H * e + 4
+    return rows * per_row + H * e
+
+
+def bwd_rows_bytes(rows, H, e, dres=False):
+    """Row pass: dy, x (+dres) read, rstd read, dx written, w read once."""
+    per_row = (4 if dres else 3) * H * e + 4
+    return rows * per_row + H * e
+
+
+def bwd_bytes(rows, H, e, dres=False):
+    """Whole backward: the row pass plus dw written."""
+    return bwd_rows_bytes(rows, H, e, dres) + H * e
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bwd_rmsnorm_fwd_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------- device plumbing
+
+class Sets:
+    """K rotating buffer sets of one workload, filled with its seeded inputs."""
+
+    def __init__(self, wl, k=None, residual=False, dres=False):
+        import numpy as np
+        import torch
+        from bwd_rmsnorm_fwd_amd import binding as B
+        from bwd_rmsnorm_fwd_amd import synth
+
+        self.wl = wl
+        rows, H = wl.rows, wl.H
+        self.e = 4 if wl.dtype == synth.F32 else 2
+        td = torch.float32 if wl.dtype == synth.F32 else torch.bfloat16
+        self.code = B.F32 if wl.dtype == synth.F32 else B.BF16
+
+        def dev(a):
+            if wl.dtype == synth.BF16:
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(td).cuda()
+            return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+        x, w, dy = dev(wl.x()), dev(wl.w()), dev(wl.dy())
+        res = dev(wl.res()) if residual else None
+        dres_t = dev(wl.dres()) if dres else None
+        n = rows * H
+        ws_bytes = max(B.rmsnorm_bwd_workspace_bytes(rows, H, self.code), 16)
+        set_bytes = n * self.e * (4 + (2 if residual else 0) + (1 if dres else 0)) + ws_bytes
+        self.k = k or max(2, math.ceil(COLD_BYTES / set_bytes))
+        self.sets = []
+        for _ in range(self.k):
+            s = {
+                "x": x.clone(), "w": w, "dy": dy.clone(),
+                "y": torch.empty((rows, H), dtype=td, device="cuda"),
+                "rstd": torch.empty(rows, dtype=torch.float32, device="cuda"),
+                "dx": torch.empty((rows, H), dtype=td, device="cuda"),
+                "dw": torch.empty(H, dtype=td, device="cuda"),
+                "ws": torch.empty(ws_bytes, dtype=torch.uint8, device="cuda"),
+            }
+            if residual:
+                s["res"] = res.clone()
+                s["h"] = torch.empty((rows, H), dtype=td, device="cuda")
+            if dres:
+                s["dres"] = dres_t.clone()
+            self.sets.append(s)
+        self.ws_bytes = ws_bytes
+        torch.cuda.synchronize()
+
+
+class Calls:
+    """Pre-marshalled C-ABI calls (pointers and sizes bound once) so that the
+    host enqueues faster than the GPU drains."""
+
+    def __init__(self, sets: Sets, stream):
+        from bwd_rmsnorm_fwd_amd import binding as B
+        self.L = B.lib()
+        wl = sets.wl
+        self.rows, self.H, self.eps, self.code = wl.rows, wl.H, ctypes.c_float(wl.eps), sets.code
+        self.stream = ctypes.c_void_p(stream.cuda_stream)
+        self.sets = sets
+
+    @staticmethod
+    def p(t):
+        return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    def fwd(self, s):
+        p = self.p
+        return (self.L.rmsnorm_fwd, (p(s["x"]), p(s["w"]), p(s["y"]), p(s["rstd"]), self.rows, self.H,
+                                     self.eps, self.code, self.stream))
+
+    def residual_fwd(self, s):
+        p = self.p
+        return (self.L.rmsnorm_residual_fwd,
+                (p(s["x"]), p(s["res"]), p(s["w"]), p(s["h"]), p(s["y"]), p(s["rstd"]), self.rows,
+                 self.H, self.eps, self.code, self.stream))
+
+    def bwd_rows(self, s, x_key="x", dres=False):
+        p = self.p
+        return (self.L.rmsnorm_bwd_rows,
+                (p(s["dy"]), p(s[x_key]), p(s["w"]), p(s["rstd"]), p(s.get("dres")) if dres else None,
+                 p(s["dx"]), p(s["ws"]), self.sets.ws_bytes, self.rows, self.H, self.eps, self.code,
+                 self.stream))
+
+    def dw_reduce(self, s):
+        p = self.p
+        return (self.L.rmsnorm_bwd_dw_reduce,
+                (p(s["ws"]), self.sets.ws_bytes, p(s["dw"]), self.rows, self.H, self.code,
+                 self.stream))
+
+    def splitrow(self, s, partials, splits):
+        p = self.p
+        return (self.L.rmsnorm_fwd_splitrow,
+                (p(s["x"]), p(s["w"]), p(s["y"]), p(s["rstd"]), p(partials), partials.numel(),
+                 self.rows, self.H, self.eps, splits, self.code, self.stream))
+
+
+def run(call):
+    fn, args = call
+    st = fn(*args)
+    if st != 0:
+        from bwd_rmsnorm_fwd_amd import binding as B
+        raise RuntimeError(f"{fn.__name__}: {B.status_str(st)}")
+
+
+# ---------------------------------------------------------------- main benchmark
+
+def bench_step(steps, warmup):
+    """The headline step on the bf16 4096 x 4096 workload."""
+    import torch
+    from bwd_rmsnorm_fwd_amd import synth
+
+    wl = synth.WORKLOADS["c2_bf16_4096x4096"]
+    sets = Sets(wl)
+    stream = torch.cuda.current_stream()
+    C = Calls(sets, stream)
+    plan = [(C.fwd(s), C.bwd_rows(s), C.dw_reduce(s)) for s in sets.sets]
+
+    for i in range(warmup):
+        f, b, r = plan[i % sets.k]
+        run(f); run(b); run(r)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        f, b, r = plan[i % sets.k]
+        e = ev[i]
+        e[0].record(stream)
+        run(f)
+        e[1].record(stream)
+        run(b)
+        e[2].record(stream)
+        run(r)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / steps
+    fwd_us = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(steps)]
+    rows_us = [ev[i][1].elapsed_time(ev[i][2]) * 1e3 for i in range(steps)]
+    red_us = [ev[i][2].elapsed_time(ev[i][3]) * 1e3 for i in range(steps)]
+    span_ms = ev[0][0].elapsed_time(ev[-1][3]) / steps
+    e = sets.e
+    fb = fwd_bytes(wl.rows, wl.H, e)
+    bb = bwd_bytes(wl.rows, wl.H, e)
+    rb = bwd_rows_bytes(wl.rows, wl.H, e)
+    return {
+        "wl": wl, "k": sets.k, "ms_step": ms_step, "span_ms": span_ms,
+        "fwd_us": statistics.mean(fwd_us), "fwd_us_median": statistics.median(fwd_us),
+        "rows_us": statistics.mean(rows_us), "rows_us_median": statistics.median(rows_us),
+        "reduce_us": statistics.mean(red_us),
+        "fwd_bytes": fb, "bwd_bytes": bb, "rows_bytes": rb,
+    }
+
+
+def cpu_baseline(min_seconds=10.0):
+    """The oracle (plain C, double, one thread) on the same workload."""
+    import numpy as np
+    import oracle
+    from bwd_rmsnorm_fwd_amd import synth
+
+    wl = synth.WORKLOADS["c2_bf16_4096x4096"]
+    x = synth.to_f64(wl.x(), wl.dtype)
+    w = synth.to_f64(wl.w(), wl.dtype)
+    dy = synth.to_f64(wl.dy(), wl.dtype)
+    oracle.rmsnorm_fwd(x[:8], w, wl.eps)  # load / build outside the timing
+    n, t0 = 0, time.perf_counter()
+    while True:
+        y, r = oracle.rmsnorm_fwd(x, w, wl.eps)
+        oracle.rmsnorm_bwd(dy, x, w, wl.eps, rstd=r)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    bytes_ = (fwd_bytes(wl.rows, wl.H, 2) + bwd_bytes(wl.rows, wl.H, 2)) * n
+    del y, np
+    return {"value": round(bytes_ / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} full passes of fwd+bwd over the bf16 4096x4096 workload "
+                      f"({el:.1f} s, inputs widened to float64, single thread)",
+            "ms_per_step": round(el * 1e3 / n, 2)}
+
+
+def load_traffic(kernel_key):
+    """HBM traffic per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    ent = d.get(kernel_key)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- suite
+
+def time_calls(calls_per_set, k, reps, warmup, stream):
+    """Per-call event timing over rotating sets: list of µs per repetition,
+    one list entry per call in the group."""
+    import torch
+    for i in range(warmup):
+        for c in calls_per_set[i % k]:
+            run(c)
+    torch.cuda.synchronize()
+    n = len(calls_per_set[0])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(reps)]
+    for i in range(reps):
+        grp = calls_per_set[i % k]
+        ev[i][0].record(stream)
+        for j, c in enumerate(grp):
+            run(c)
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    return [[ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(reps)] for j in range(n)]
+
+
+def summarise(name, us, nbytes, extra=None):
+    med = statistics.median(us)
+    p95 = sorted(us)[min(len(us) - 1, int(0.95 * len(us)))]
+    gbs = nbytes / (med * 1e-6) / 1e9
+    d = {"name": name, "us_median": round(med, 3), "us_p95": round(p95, 3),
+         "us_mean": round(statistics.mean(us), 3), "bytes": nbytes, "GB_s": round(gbs, 1),
+         "pct_peak": round(100 * gbs / PEAK_GBS, 2)}
+    if extra:
+        d.update(extra)
+    return d
+
+
+def suite(path, reps=200, warmup=20):
+    import torch
+    from bwd_rmsnorm_fwd_amd import synth
+
+    stream = torch.cuda.current_stream()
+    out = []
+
+    def emit(d):
+        out.append(d)
+        print(json.dumps(d), file=sys.stderr, flush=True)
+
+    for name in ["c1_f32_64x896", "c2_bf16_4096x4096", "c5a_bf16_262144x128",
+                 "c5b_bf16_8192x8192"]:
+        wl = synth.WORKLOADS[name]
+        sets = Sets(wl)
+        C = Calls(sets, stream)
+        e = sets.e
+        groups = [(C.fwd(s), C.bwd_rows(s), C.dw_reduce(s)) for s in sets.sets]
+        tf, tr, td = time_calls(groups, sets.k, reps, warmup, stream)
+        tb = [a + b for a, b in zip(tr, td)]
+        meta = {"workload": name, "cold_sets": sets.k}
+        emit(summarise(f"{name}/fwd", tf, fwd_bytes(wl.rows, wl.H, e), meta))
+        emit(summarise(f"{name}/bwd_rows", tr, bwd_rows_bytes(wl.rows, wl.H, e), meta))
+        emit(summarise(f"{name}/dw_reduce", td, wl.H * e, meta))
+        emit(summarise(f"{name}/bwd", tb, bwd_bytes(wl.rows, wl.H, e), meta))
+        # Warm-cache forward (same buffers every call): labelled, not HBM.
+        (wf,) = time_calls([(C.fwd(sets.sets[0]),)], 1, reps, warmup, stream)
+        emit(summarise(f"{name}/fwd_warm_cache", wf, fwd_bytes(wl.rows, wl.H, e),
+                       {"workload": name, "note": "same buffers each call; not HBM-bound"}))
+        del sets, C, groups
+        torch.cuda.empty_cache()
+
+    wl = synth.WORKLOADS["c4_bf16_residual_16384x4096"]
+    sets = Sets(wl, residual=True, dres=True)
+    C = Calls(sets, stream)
+    groups = [(C.residual_fwd(s), C.bwd_rows(s, x_key="h", dres=True), C.dw_reduce(s))
+              for s in sets.sets]
+    tf, tr, td = time_calls(groups, sets.k, reps, warmup, stream)
+    tb = [a + b for a, b in zip(tr, td)]
+    meta = {"workload": wl.name, "cold_sets": sets.k}
+    emit(summarise(f"{wl.name}/residual_fwd", tf, fwd_bytes(wl.rows, wl.H, 2, residual=True), meta))
+    emit(summarise(f"{wl.name}/bwd_rows_dres", tr, bwd_rows_bytes(wl.rows, wl.H, 2, dres=True), meta))
+    emit(summarise(f"{wl.name}/bwd_dres", tb, bwd_bytes(wl.rows, wl.H, 2, dres=True), meta))
+    del sets, C, groups
+    torch.cuda.empty_cache()
+
+    # Decode: 10k back-to-back calls on one stream, µs per call.
+    wl = synth.WORKLOADS["c3_bf16_decode_1x896"]
+    sets = Sets(wl, k=1)
+    C = Calls(sets, stream)
+    s = sets.sets[0]
+    ncalls = 10000
+    for splits in (0, 1, 4, 8, 16):
+        if splits == 0:
+            call = C.fwd(s)
+            label = "row_kernel"
+        else:
+            partials = torch.empty(splits, dtype=torch.float32, device="cuda")
+            call = C.splitrow(s, partials, splits)
+            label = f"splitrow_S{splits}"
+        for _ in range(200):
+            run(call)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(ncalls):
+            run(call)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / ncalls
+        emit({"name": f"{wl.name}/{label}", "us_per_call": round(us, 3), "calls": ncalls,
+              "launches_per_call": 1 if splits == 0 else 2,
+              "bytes": fwd_bytes(1, wl.H, 2), "workload": wl.name})
+    with open(path, "w") as f:
+        for d in out:
+            f.write(json.dumps(d) + "\n")
+
+
+# ---------------------------------------------------------------- entry
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--suite", default=None, help="also measure every workload into this file")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the RMSNorm path here is built and timed on a single "
+              "MI355X (rows shard across GPUs with no exchange except one dw all-reduce, which "
+              "this build does not implement); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.init()
+    r = bench_step(args.steps, args.warmup)
+    wl = r["wl"]
+    total_bytes = r["fwd_bytes"] + r["bwd_bytes"]
+    value = total_bytes / (r["ms_step"] * 1e-3) / 1e9
+    ach = r["rows_bytes"] / (r["rows_us"] * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "rmsnorm fwd+bwd bf16 rows=4096 H=4096 eps=1e-6 "
+                               "(x~N(0,1) with 41 outlier feature columns x50, w~U(0.5,1.5), "
+                               "dy~N(0,1e-2))",
+                   "rows": wl.rows, "H": wl.H, "cold_cache_buffer_sets": r["k"],
+                   "bytes_per_step": total_bytes},
+        "pct_of_peak": round(100 * value / PEAK_GBS, 2),
+        "fwd_us": round(r["fwd_us"], 3),
+        "bwd_us": round(r["rows_us"] + r["reduce_us"], 3),
+        "bwd_rows_us": round(r["rows_us"], 3),
+        "dw_reduce_us": round(r["reduce_us"], 3),
+        "event_span_ms_per_step": round(r["span_ms"], 5),
+        "roofline": {
+            "kernel": "bwd_rows_kernel<bf16,8,256,2,512>",
+            "bound": "hbm",
+            "achieved": round(ach, 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(ach / PEAK_GBS, 4),
+            "traffic": load_traffic("bwd_rows_c2"),
+            "algorithmic_bytes_per_launch": r["rows_bytes"],
+            "avg_launch_us": round(r["rows_us"], 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    if args.suite:
+        suite(args.suite)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,59 @@
+"""Build librmsnorm_mi355x.so from csrc/ with hipcc for gfx950 (in-tree).
+
+Each translation unit is compiled to an object in parallel, then linked into
+one shared library next to this file.  Extra -D definitions (kernel tuning
+constants) can be passed through ``defines``.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+LIB_NAME = "librmsnorm_mi355x.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+SOURCES = ["rmsnorm_api.hip", "rmsnorm_fwd.hip", "rmsnorm_bwd.hip", "rmsnorm_split.hip"]
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-fno-gpu-flush-denormals-to-zero",
+    # Keep packed fp32 instructions out of the generated code.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(out_path: str = LIB_PATH, defines=(), build_dir: str | None = None, jobs: int = 8,
+          verbose: bool = False) -> str:
+    build_dir = build_dir or os.path.join(PKG, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
+
+    def compile_one(src):
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        if verbose and (r.stdout.strip() or r.stderr.strip()):
+            print(r.stderr)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = out_path + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out_path)
+    return out_path
+
+
+if __name__ == "__main__":
+    import sys
+    print(build(defines=sys.argv[1:], verbose=True))

@@ -1,0 +1,208 @@
+// Device helpers shared by the RMSNorm kernels (gfx950 / CDNA4, wave64).
+//
+// Layout conventions used by every row kernel:
+//   * A row of H elements is handled by a "team" of TEAM lanes.  TEAM <= 64
+//     keeps the team inside one wavefront (several rows per wavefront when
+//     TEAM < 64); TEAM > 64 spans TEAM/64 wavefronts of one workgroup.
+//   * Each lane owns NCH chunks of VEC consecutive elements; chunk c of lane l
+//     starts at column (c * TEAM + l) * VEC, so a team's loads of one chunk
+//     are contiguous (128-bit per lane when VEC * sizeof(T) == 16).
+//   * Columns >= H are masked: they load as zero and are never stored, so
+//     they add nothing to any sum (the mean still divides by H).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rms {
+
+using bf16_t = uint16_t;  // storage of one bfloat16
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Element I/O: VEC elements of T <-> VEC floats.
+
+template <typename T, int VEC>
+struct Pack;  // raw storage of VEC elements
+
+template <> struct Pack<float, 4> { uint4 v; };
+template <> struct Pack<float, 1> { float v; };
+template <> struct Pack<bf16_t, 8> { uint4 v; };
+template <> struct Pack<bf16_t, 1> { bf16_t v; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Round two floats to bfloat16 (nearest even; gfx950 converts natively) and pack.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    __bf16 ha = (__bf16)a;
+    __bf16 hb = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+__device__ __forceinline__ float round_to(float v, float*) { return v; }
+__device__ __forceinline__ float round_to(float v, bf16_t*) {
+    return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v) << 16);
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ Pack<T, VEC> load_pack(const T* p) {
+    Pack<T, VEC> r;
+    if constexpr (VEC == 1) {
+        r.v = *p;
+    } else {
+        r.v = *reinterpret_cast<const uint4*>(p);
+    }
+    return r;
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ Pack<T, VEC> zero_pack() {
+    Pack<T, VEC> r;
+    if constexpr (VEC == 1) {
+        r.v = 0;
+    } else {
+        r.v = make_uint4(0, 0, 0, 0);
+    }
+    return r;
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void unpack(const Pack<T, VEC>& p, float (&f)[VEC]) {
+    if constexpr (sizeof(T) == 4 && VEC == 4) {
+        f[0] = __uint_as_float(p.v.x); f[1] = __uint_as_float(p.v.y);
+        f[2] = __uint_as_float(p.v.z); f[3] = __uint_as_float(p.v.w);
+    } else if constexpr (sizeof(T) == 4 && VEC == 1) {
+        f[0] = p.v;
+    } else if constexpr (VEC == 8) {
+        f[0] = bf16_lo(p.v.x); f[1] = bf16_hi(p.v.x);
+        f[2] = bf16_lo(p.v.y); f[3] = bf16_hi(p.v.y);
+        f[4] = bf16_lo(p.v.z); f[5] = bf16_hi(p.v.z);
+        f[6] = bf16_lo(p.v.w); f[7] = bf16_hi(p.v.w);
+    } else {
+        f[0] = __uint_as_float((uint32_t)p.v << 16);
+    }
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void store_vec(T* p, const float (&f)[VEC]) {
+    if constexpr (sizeof(T) == 4 && VEC == 4) {
+        *reinterpret_cast<uint4*>(p) = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                                                  __float_as_uint(f[2]), __float_as_uint(f[3]));
+    } else if constexpr (sizeof(T) == 4 && VEC == 1) {
+        *reinterpret_cast<float*>(p) = f[0];
+    } else if constexpr (VEC == 8) {
+        *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                                  pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    } else {
+        *p = __builtin_bit_cast(uint16_t, (__bf16)f[0]);
+    }
+}
+
+// Products for the per-row fp64 sums.  For bf16 inputs the fp32 products are
+// exact (8-bit significands: a square has 16 bits, w*dy*x has 24), so the
+// fp32 multiply loses nothing; for fp32 inputs they are formed in fp64.
+__device__ __forceinline__ double sq64(float v, float*) { return (double)v * (double)v; }
+__device__ __forceinline__ double sq64(float v, bf16_t*) { return (double)(v * v); }
+__device__ __forceinline__ double prod3_64(float a, float b, float c, float*) {
+    return (double)a * (double)b * (double)c;
+}
+__device__ __forceinline__ double prod3_64(float a, float b, float c, bf16_t*) {
+    return (double)((a * b) * c);
+}
+
+// ---------------------------------------------------------------------------
+// Team all-reductions.  Every lane of a team ends with the bitwise-identical
+// sum (each step adds a value to its partner's, a + b == b + a exactly).
+// All 64 lanes of the wavefront must be active.
+
+// DPP controls (GFX9 encoding).
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7-i within 8 lanes
+constexpr int kRowMirror = 0x140;      // lane i <-> 15-i within 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    int2 p = __builtin_bit_cast(int2, v);
+    p.x = __builtin_amdgcn_update_dpp(0, p.x, CTRL, 0xF, 0xF, false);
+    p.y = __builtin_amdgcn_update_dpp(0, p.y, CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, p);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    int2 p = __builtin_bit_cast(int2, v);
+    p.x = __builtin_amdgcn_readlane(p.x, lane);
+    p.y = __builtin_amdgcn_readlane(p.y, lane);
+    return __builtin_bit_cast(double, p);
+}
+
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over aligned groups of TEAM lanes (TEAM in 1..64, a power of two).
+template <int TEAM, typename V>
+__device__ __forceinline__ V team_sum_wave(V v) {
+    static_assert(TEAM >= 1 && TEAM <= 64 && (TEAM & (TEAM - 1)) == 0, "TEAM");
+    auto step = [](V a, auto ctrl_tag) {
+        constexpr int C = decltype(ctrl_tag)::value;
+        if constexpr (sizeof(V) == 8) return a + dpp_f64<C>(a);
+        else return a + dpp_f32<C>(a);
+    };
+    if constexpr (TEAM >= 2) v = step(v, std::integral_constant<int, kQuadXor1>{});
+    if constexpr (TEAM >= 4) v = step(v, std::integral_constant<int, kQuadXor2>{});
+    if constexpr (TEAM >= 8) v = step(v, std::integral_constant<int, kRowHalfMirror>{});
+    if constexpr (TEAM >= 16) v = step(v, std::integral_constant<int, kRowMirror>{});
+    if constexpr (TEAM >= 32) {
+        // Rows of 16 lanes now hold their sums; combine rows through
+        // lane reads (uniform values) in a fixed order.
+        V s0, s1, s2, s3;
+        if constexpr (sizeof(V) == 8) {
+            s0 = readlane_f64(v, 0); s1 = readlane_f64(v, 16);
+            s2 = readlane_f64(v, 32); s3 = readlane_f64(v, 48);
+        } else {
+            s0 = readlane_f32(v, 0); s1 = readlane_f32(v, 16);
+            s2 = readlane_f32(v, 32); s3 = readlane_f32(v, 48);
+        }
+        if constexpr (TEAM == 64) {
+            v = (s0 + s1) + (s2 + s3);
+        } else {
+            const bool upper = (threadIdx.x & 32) != 0;
+            v = upper ? (s2 + s3) : (s0 + s1);
+        }
+    }
+    return v;
+}
+
+// Sum over a team of TEAM lanes; TEAM > 64 spans TEAM/64 wavefronts and uses
+// `lds` (at least TEAM/64 values per team).  Contains __syncthreads() when
+// TEAM > 64, so every thread of the workgroup must call it.
+template <int TEAM, typename V>
+__device__ __forceinline__ V team_sum(V v, V* lds) {
+    if constexpr (TEAM <= 64) {
+        return team_sum_wave<TEAM>(v);
+    } else {
+        constexpr int NW = TEAM / kWave;
+        v = team_sum_wave<64>(v);
+        const int lt = threadIdx.x % TEAM;
+        const int team = threadIdx.x / TEAM;
+        V* slot = lds + team * NW;
+        if ((lt & (kWave - 1)) == 0) slot[lt / kWave] = v;
+        __syncthreads();
+        V s = slot[0];
+#pragma unroll
+        for (int k = 1; k < NW; ++k) s += slot[k];
+        __syncthreads();  // slots may be reused by the next reduction
+        return s;
+    }
+}
+
+}  // namespace rms

@@ -1,0 +1,70 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+// Arguments are validated by the caller; these functions only pick a
+// kernel instance and launch it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rms {
+
+enum class DType { F32 = 0, BF16 = 1 };
+
+// Geometry chosen for a row width: a team of `team` lanes handles one row,
+// each lane holds `nch` chunks of `vec` elements.
+struct Geometry {
+    int vec;
+    int team;
+    int nch;
+    int wg;    // workgroup size
+    int rpw;   // rows per workgroup iteration = wg / team
+};
+
+// Returns false when H needs more than the largest register tile.
+bool choose_geometry(int64_t H, int vec, Geometry* g);
+
+// Largest vector width usable for these pointers and H (elements; 16 bytes
+// worth when everything is aligned, else 1).
+int choose_vec(DType dt, int64_t H, const void* const* ptrs, int nptrs);
+
+struct FwdArgs {
+    const void* x;
+    const void* res;  // residual variant only
+    const void* w;
+    void* h;          // residual variant only
+    void* y;
+    float* rstd;      // may be null
+    int64_t rows;
+    int H;
+    float eps;
+};
+
+struct BwdArgs {
+    const void* dy;
+    const void* x;
+    const void* w;
+    const float* rstd;  // null: recompute
+    const void* dres;   // may be null
+    void* dx;
+    float* partial;     // [G][ldp] fp32
+    int64_t rows;
+    int H;
+    int ldp;            // partial row stride (floats)
+    int G;              // workgroups of the row pass
+    float eps;
+};
+
+// Number of workgroups of the backward row pass and the partial row stride.
+// Pure functions of (rows, H, dtype, vec): the reduction order, and so the
+// bits of dw, depend on nothing else.
+int bwd_groups(int64_t rows, int64_t H, DType dt);
+int partial_ld(int64_t H);
+
+hipError_t launch_fwd(DType dt, int vec, const FwdArgs& a, bool residual, hipStream_t s);
+hipError_t launch_bwd_rows(DType dt, int vec, const BwdArgs& a, hipStream_t s);
+hipError_t launch_dw_reduce(DType dt, const float* partial, int G, int ldp, int H, void* dw,
+                            hipStream_t s);
+hipError_t launch_splitrow(DType dt, int vec, const FwdArgs& a, float* partials, int splits,
+                           hipStream_t s);
+
+}  // namespace rms

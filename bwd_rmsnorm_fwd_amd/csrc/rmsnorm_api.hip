@@ -1,0 +1,235 @@
+// C ABI of the RMSNorm library: argument validation, geometry and vector
+// width selection, and launches on the caller's stream.  No allocation, no
+// host synchronisation, no printing.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/rmsnorm.h"
+#include "launch.hpp"
+
+namespace rms {
+
+bool choose_geometry(int64_t H, int vec, Geometry* g) {
+    const int64_t n = (H + vec - 1) / vec;  // vectors per row
+    int team, nch;
+    if (n <= 64) {
+        team = 1;
+        while (team < n) team *= 2;
+        nch = 1;
+    } else if (n <= 128) { team = 64; nch = 2; }
+    else if (n <= 256) { team = 128; nch = 2; }
+    else if (n <= 512) { team = 256; nch = 2; }
+    else if (n <= 1024) { team = 512; nch = 2; }
+    else if (n <= 2048) { team = 1024; nch = 2; }
+    else if (n <= 4096) { team = 1024; nch = 4; }
+    else if (n <= 8192) { team = 1024; nch = 8; }
+    else if (n <= 16384) { team = 1024; nch = 16; }
+    else return false;
+    g->vec = vec;
+    g->team = team;
+    g->nch = nch;
+    g->wg = team > 256 ? team : 256;
+    g->rpw = g->wg / team;
+    return true;
+}
+
+static size_t elem_size(DType dt) { return dt == DType::F32 ? 4 : 2; }
+
+int choose_vec(DType dt, int64_t H, const void* const* ptrs, int nptrs) {
+    const size_t e = elem_size(dt);
+    const int full = (int)(16 / e);
+    if ((H * (int64_t)e) % 16 != 0) return 1;
+    for (int i = 0; i < nptrs; ++i)
+        if (ptrs[i] && ((uintptr_t)ptrs[i] % 16) != 0) return 1;
+    return full;
+}
+
+}  // namespace rms
+
+using rms::DType;
+
+namespace {
+
+bool valid_dtype(rmsnorm_dtype_t dt) { return dt == RMSNORM_F32 || dt == RMSNORM_BF16; }
+DType to_dt(rmsnorm_dtype_t dt) { return dt == RMSNORM_F32 ? DType::F32 : DType::BF16; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Common checks on shape, eps and dtype.
+rmsnorm_status_t check_shape(int64_t rows, int64_t H, float eps, rmsnorm_dtype_t dt) {
+    if (!valid_dtype(dt)) return RMSNORM_EINVAL;
+    if (rows < 0 || H < 1) return RMSNORM_EINVAL;
+    if (!(eps >= 0.0f) || isinf(eps)) return RMSNORM_EINVAL;
+    if (H > RMSNORM_MAX_H) return RMSNORM_EUNSUPPORTED;
+    if (rows > (int64_t)INT32_MAX * 64) return RMSNORM_EUNSUPPORTED;
+    return RMSNORM_OK;
+}
+
+// Vector width for these pointers, or 0 when H is too wide for that width.
+int pick_vec(DType dt, int64_t H, const void* const* ptrs, int n) {
+    int vec = rms::choose_vec(dt, H, ptrs, n);
+    rms::Geometry g;
+    if (!rms::choose_geometry(H, vec, &g)) return 0;
+    return vec;
+}
+
+rmsnorm_status_t launch_status(hipError_t e) {
+    return e == hipSuccess ? RMSNORM_OK : RMSNORM_ELAUNCH;
+}
+
+size_t bwd_workspace(int64_t rows, int64_t H, DType dt) {
+    const int G = rms::bwd_groups(rows, H, dt);
+    return (size_t)G * (size_t)rms::partial_ld(H) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rmsnorm_status_str(rmsnorm_status_t status) {
+    switch (status) {
+        case RMSNORM_OK: return "ok";
+        case RMSNORM_EINVAL: return "invalid argument";
+        case RMSNORM_EALIGN: return "pointer not aligned to its element size";
+        case RMSNORM_EWORKSPACE: return "workspace missing or too small";
+        case RMSNORM_EUNSUPPORTED: return "unsupported shape";
+        case RMSNORM_ELAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+static rmsnorm_status_t fwd_common(const void* x, const void* res, const void* w, void* h, void* y,
+                                   float* rstd, int64_t rows, int64_t H, float eps,
+                                   rmsnorm_dtype_t dtype, hipStream_t stream, bool residual) {
+    rmsnorm_status_t st = check_shape(rows, H, eps, dtype);
+    if (st != RMSNORM_OK) return st;
+    if (rows == 0) return RMSNORM_OK;
+    if (!x || !w || !y) return RMSNORM_EINVAL;
+    if (residual && (!res || !h)) return RMSNORM_EINVAL;
+    const DType dt = to_dt(dtype);
+    const size_t e = dtype == RMSNORM_F32 ? 4 : 2;
+    if (!aligned(x, e) || !aligned(w, e) || !aligned(y, e) || (rstd && !aligned(rstd, 4)))
+        return RMSNORM_EALIGN;
+    if (residual && (!aligned(res, e) || !aligned(h, e))) return RMSNORM_EALIGN;
+    const void* ptrs[5] = {x, w, y, res, h};
+    const int vec = pick_vec(dt, H, ptrs, 5);
+    if (!vec) return RMSNORM_EUNSUPPORTED;
+    rms::FwdArgs a{x, res, w, h, y, rstd, rows, (int)H, eps};
+    return launch_status(rms::launch_fwd(dt, vec, a, residual, stream));
+}
+
+rmsnorm_status_t rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd, int64_t rows,
+                             int64_t H, float eps, rmsnorm_dtype_t dtype, hipStream_t stream) {
+    return fwd_common(x, nullptr, w, nullptr, y, rstd, rows, H, eps, dtype, stream, false);
+}
+
+rmsnorm_status_t rmsnorm_residual_fwd(const void* x, const void* res, const void* w, void* h,
+                                      void* y, float* rstd, int64_t rows, int64_t H, float eps,
+                                      rmsnorm_dtype_t dtype, hipStream_t stream) {
+    return fwd_common(x, res, w, h, y, rstd, rows, H, eps, dtype, stream, true);
+}
+
+size_t rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t H, rmsnorm_dtype_t dtype) {
+    if (check_shape(rows, H, 0.0f, dtype) != RMSNORM_OK) return 0;
+    return bwd_workspace(rows, H, to_dt(dtype));
+}
+
+static rmsnorm_status_t bwd_rows_common(const void* dy, const void* x, const void* w,
+                                        const float* rstd, const void* dres, void* dx,
+                                        void* workspace, size_t workspace_bytes, int64_t rows,
+                                        int64_t H, float eps, rmsnorm_dtype_t dtype,
+                                        hipStream_t stream) {
+    const DType dt = to_dt(dtype);
+    if (!dy || !x || !w || !dx) return RMSNORM_EINVAL;
+    const size_t e = dtype == RMSNORM_F32 ? 4 : 2;
+    if (!aligned(dy, e) || !aligned(x, e) || !aligned(w, e) || !aligned(dx, e) ||
+        (dres && !aligned(dres, e)) || (rstd && !aligned(rstd, 4)))
+        return RMSNORM_EALIGN;
+    const size_t need = bwd_workspace(rows, H, dt);
+    if (!workspace || workspace_bytes < need) return RMSNORM_EWORKSPACE;
+    if (!aligned(workspace, 16)) return RMSNORM_EALIGN;
+    const void* ptrs[5] = {dy, x, w, dx, dres};
+    const int vec = pick_vec(dt, H, ptrs, 5);
+    if (!vec) return RMSNORM_EUNSUPPORTED;
+    rms::BwdArgs a{dy, x, w, rstd, dres, dx, (float*)workspace, rows, (int)H,
+                   rms::partial_ld(H), rms::bwd_groups(rows, H, dt), eps};
+    return launch_status(rms::launch_bwd_rows(dt, vec, a, stream));
+}
+
+static rmsnorm_status_t dw_reduce_common(const void* workspace, size_t workspace_bytes, void* dw,
+                                         int64_t rows, int64_t H, rmsnorm_dtype_t dtype,
+                                         hipStream_t stream) {
+    const DType dt = to_dt(dtype);
+    if (!dw) return RMSNORM_EINVAL;
+    if (!aligned(dw, dtype == RMSNORM_F32 ? 4 : 2)) return RMSNORM_EALIGN;
+    const size_t need = bwd_workspace(rows, H, dt);
+    if (need && (!workspace || workspace_bytes < need)) return RMSNORM_EWORKSPACE;
+    if (need && !aligned(workspace, 16)) return RMSNORM_EALIGN;
+    return launch_status(rms::launch_dw_reduce(dt, (const float*)workspace,
+                                               rms::bwd_groups(rows, H, dt), rms::partial_ld(H),
+                                               (int)H, dw, stream));
+}
+
+rmsnorm_status_t rmsnorm_bwd_rows(const void* dy, const void* x, const void* w, const float* rstd,
+                                  const void* dres, void* dx, void* workspace,
+                                  size_t workspace_bytes, int64_t rows, int64_t H, float eps,
+                                  rmsnorm_dtype_t dtype, hipStream_t stream) {
+    rmsnorm_status_t st = check_shape(rows, H, eps, dtype);
+    if (st != RMSNORM_OK) return st;
+    if (rows < 1) return RMSNORM_EINVAL;
+    return bwd_rows_common(dy, x, w, rstd, dres, dx, workspace, workspace_bytes, rows, H, eps,
+                           dtype, stream);
+}
+
+rmsnorm_status_t rmsnorm_bwd_dw_reduce(const void* workspace, size_t workspace_bytes, void* dw,
+                                       int64_t rows, int64_t H, rmsnorm_dtype_t dtype,
+                                       hipStream_t stream) {
+    rmsnorm_status_t st = check_shape(rows, H, 0.0f, dtype);
+    if (st != RMSNORM_OK) return st;
+    return dw_reduce_common(workspace, workspace_bytes, dw, rows, H, dtype, stream);
+}
+
+rmsnorm_status_t rmsnorm_bwd(const void* dy, const void* x, const void* w, const float* rstd,
+                             const void* dres, void* dx, void* dw, void* workspace,
+                             size_t workspace_bytes, int64_t rows, int64_t H, float eps,
+                             rmsnorm_dtype_t dtype, hipStream_t stream) {
+    rmsnorm_status_t st = check_shape(rows, H, eps, dtype);
+    if (st != RMSNORM_OK) return st;
+    if (!dw) return RMSNORM_EINVAL;
+    if (rows > 0) {
+        // Validate the reduce pass's arguments too before enqueuing anything.
+        if (!aligned(dw, dtype == RMSNORM_F32 ? 4 : 2)) return RMSNORM_EALIGN;
+        st = bwd_rows_common(dy, x, w, rstd, dres, dx, workspace, workspace_bytes, rows, H, eps,
+                             dtype, stream);
+        if (st != RMSNORM_OK) return st;
+    }
+    return dw_reduce_common(workspace, workspace_bytes, dw, rows, H, dtype, stream);
+}
+
+size_t rmsnorm_splitrow_partials_count(int64_t rows, int splits) {
+    if (rows < 0 || splits < 1 || splits > RMSNORM_MAX_SPLITS) return 0;
+    return (size_t)rows * (size_t)splits;
+}
+
+rmsnorm_status_t rmsnorm_fwd_splitrow(const void* x, const void* w, void* y, float* rstd,
+                                      float* partials, size_t partials_count, int64_t rows,
+                                      int64_t H, float eps, int splits, rmsnorm_dtype_t dtype,
+                                      hipStream_t stream) {
+    rmsnorm_status_t st = check_shape(rows, H, eps, dtype);
+    if (st != RMSNORM_OK) return st;
+    if (rows < 1 || splits < 1 || splits > RMSNORM_MAX_SPLITS) return RMSNORM_EINVAL;
+    if (rows > INT32_MAX) return RMSNORM_EUNSUPPORTED;
+    if (!x || !w || !y) return RMSNORM_EINVAL;
+    if (!partials || partials_count < (size_t)rows * (size_t)splits) return RMSNORM_EWORKSPACE;
+    const DType dt = to_dt(dtype);
+    const size_t e = dtype == RMSNORM_F32 ? 4 : 2;
+    if (!aligned(x, e) || !aligned(w, e) || !aligned(y, e) || (rstd && !aligned(rstd, 4)) ||
+        !aligned(partials, 4))
+        return RMSNORM_EALIGN;
+    const void* ptrs[3] = {x, w, y};
+    const int vec = rms::choose_vec(dt, H, ptrs, 3);
+    rms::FwdArgs a{x, nullptr, w, nullptr, y, rstd, rows, (int)H, eps};
+    return launch_status(rms::launch_splitrow(dt, vec, a, partials, splits, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,330 @@
+// Backward RMSNorm for gfx950: a row pass (dx and per-workgroup dw partial
+// column sums) and a dw reduce pass.
+//
+// P1 = "训推加速 Qwen3 实战：从“调包”到手写 Triton Kernel（含 backward）":
+//   §5.3 wdy = w*dy, c = (1/H) sum_j wdy_j x_j, dx = r (wdy - x r^2 c),
+//   dw_j = sum over rows of dy_j x_j r; §5.4 dw in two passes (per-program
+//   partials, then a cross-row sum) rather than atomics, whose ordering makes
+//   results jitter; §5.6 reductions in fp32, not bf16.
+// P2 = trdm.cn/news/483216: §3.3 fixed-order merge of fp32 partials for
+//   run-to-run reproducibility.
+//
+// Design (MI355X):
+//   * Row pass: G persistent workgroups; workgroup g owns a contiguous range
+//     of rows, processed R rows at a time (one team per row, as in the
+//     forward), prefetching the next R rows while finishing the current.
+//     dy, x (and dres) are read once; rstd is the forward's saved statistic
+//     (or is recomputed from x when none is given).
+//   * The row sums c (and sum x^2 when recomputing) are exact fp32 products
+//     (for bf16 inputs) accumulated in fp64, so c and r carry no cancellation
+//     error.  dx uses k = r^2 c split into two floats, k_hi + k_lo, applied
+//     with two fused multiply-adds: wdy - x k is formed with one rounding,
+//     which keeps dx accurate where its two terms nearly cancel.
+//   * dw: each lane keeps fp32 column sums for its columns over the
+//     workgroup's rows; the R teams are combined through LDS in team order,
+//     and the workgroup writes one partial row.  The reduce pass adds the G
+//     partial rows per column in a fixed order.  No atomics anywhere.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace rms {
+
+template <typename T, int VEC, int TEAM, int NCH, int WG, bool DRES>
+__global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __restrict__ x,
+                                                      const T* __restrict__ w,
+                                                      const float* __restrict__ rstd,
+                                                      const T* dres, T* dx,
+                                                      float* __restrict__ partial, int64_t rows,
+                                                      int H, int ldp, int64_t rpg, float eps) {
+    constexpr int R = WG / TEAM;
+    constexpr int NWT = TEAM > kWave ? TEAM / kWave : 1;
+    constexpr int HT = TEAM * NCH * VEC;  // columns covered by one team
+    constexpr int E = NCH * VEC;          // elements per lane
+    // Register budget: w cached and the next rows prefetched unless the
+    // per-lane tile is large for this workgroup size.
+    constexpr bool kCacheW = E * WG <= 8192;
+    constexpr bool kPrefetch = E * WG <= 8192;
+    // Teams combine their dw sums either side by side ([R][HT], summed per
+    // column in team order) when that fits in 32 KiB, or one after another
+    // into a single [HT] row.
+    constexpr bool kWideComb = R > 1 && R * HT <= 8192;
+    __shared__ double red[TEAM > kWave ? 2 * R * NWT : 1];
+    __shared__ float comb[R == 1 ? 1 : (kWideComb ? R * HT : HT)];
+
+    const int tid = threadIdx.x;
+    const int team = tid / TEAM;
+    const int lt = tid % TEAM;
+    const bool has_rstd = rstd != nullptr;
+    const int64_t begin = (int64_t)blockIdx.x * rpg;
+    const int64_t end = begin + rpg < rows ? begin + rpg : rows;
+
+    float wv[kCacheW ? NCH : 1][VEC];
+    float acc[NCH][VEC];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        if constexpr (kCacheW) {
+            const int col = (c * TEAM + lt) * VEC;
+            Pack<T, VEC> p = col < H ? load_pack<T, VEC>(w + col) : zero_pack<T, VEC>();
+            unpack(p, wv[c]);
+        }
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[c][k] = 0.f;
+    }
+    auto weights = [&](int c, float (&wc)[VEC]) {
+        if constexpr (kCacheW) {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) wc[k] = wv[c][k];
+        } else {
+            const int col = (c * TEAM + lt) * VEC;
+            unpack(col < H ? load_pack<T, VEC>(w + col) : zero_pack<T, VEC>(), wc);
+        }
+    };
+
+    struct RowRegs {
+        Pack<T, VEC> x[NCH], dy[NCH], dr[DRES ? NCH : 1];
+        float rs;
+    };
+    auto load_row = [&](int64_t base, RowRegs& q) {
+        const int64_t row = base + team;
+        const bool active = row < end;
+        const int64_t off = row * (int64_t)H;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int col = (c * TEAM + lt) * VEC;
+            const bool ok = active && col < H;
+            q.x[c] = ok ? load_pack<T, VEC>(x + off + col) : zero_pack<T, VEC>();
+            q.dy[c] = ok ? load_pack<T, VEC>(dy + off + col) : zero_pack<T, VEC>();
+            if constexpr (DRES)
+                q.dr[c] = ok ? load_pack<T, VEC>(dres + off + col) : zero_pack<T, VEC>();
+        }
+        q.rs = (active && has_rstd) ? rstd[row] : 0.f;
+    };
+
+    RowRegs cur;
+    int64_t base = begin;
+    if (kPrefetch && base < end) load_row(base, cur);
+    while (base < end) {
+        const int64_t nb = base + R;
+        RowRegs nxt;
+        if constexpr (kPrefetch) {
+            if (nb < end) load_row(nb, nxt);
+        } else {
+            load_row(base, cur);
+        }
+
+        const int64_t row = base + team;
+        const bool active = row < end;
+        // Pass A: row sums.  Values are unpacked again in pass B rather than
+        // kept live across the reduction (unpacking is a shift or a mask).
+        double cs = 0.0, ss = 0.0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            float xv[VEC], dyv[VEC], wc[VEC];
+            unpack(cur.x[c], xv);
+            unpack(cur.dy[c], dyv);
+            weights(c, wc);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                cs += prod3_64(wc[k], dyv[k], xv[k], (T*)nullptr);
+                if (!has_rstd) ss += sq64(xv[k], (T*)nullptr);
+            }
+        }
+        cs = team_sum<TEAM>(cs, red);
+        double r;
+        if (has_rstd) {
+            r = (double)cur.rs;
+        } else {
+            ss = team_sum<TEAM>(ss, red + R * NWT);
+            r = 1.0 / sqrt(ss / (double)H + (double)eps);
+        }
+        const float rf = (float)r;
+        const double kk = r * r * (cs / (double)H);
+        const float k_hi = (float)kk;
+        const float k_lo = (float)(kk - (double)k_hi);
+        // Pass B: dx and the dw column sums.
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            float xv[VEC], dyv[VEC], wc[VEC], o[VEC];
+            unpack(cur.x[c], xv);
+            unpack(cur.dy[c], dyv);
+            weights(c, wc);
+            if constexpr (DRES) {
+                // dx and the residual-stream gradient can cancel; form
+                // r * (wdy - x k) + dres in fp64 and round once.
+                float drv[VEC];
+                unpack(cur.dr[c], drv);
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float wdy = wc[k] * dyv[k];
+                    const double t = __builtin_fma(-(double)xv[k], kk, (double)wdy);
+                    o[k] = (float)__builtin_fma(r, t, (double)drv[k]);
+                    acc[c][k] += (dyv[k] * xv[k]) * rf;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float wdy = wc[k] * dyv[k];
+                    float t = __builtin_fmaf(-xv[k], k_hi, wdy);
+                    t = __builtin_fmaf(-xv[k], k_lo, t);
+                    o[k] = rf * t;
+                    acc[c][k] += (dyv[k] * xv[k]) * rf;
+                }
+            }
+            const int col = (c * TEAM + lt) * VEC;
+            if (active && col < H) store_vec<T, VEC>(dx + row * (int64_t)H + col, o);
+        }
+
+        if constexpr (kPrefetch) cur = nxt;
+        base = nb;
+    }
+
+    // One partial row per workgroup: combine the R teams in team order.
+    float* prow = partial + (int64_t)blockIdx.x * ldp;
+    if constexpr (R == 1) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int col = (c * TEAM + lt) * VEC;
+            if (col < H) {
+                if constexpr (VEC == 1) {
+                    prow[col] = acc[c][0];
+                } else {
+#pragma unroll
+                    for (int k = 0; k < VEC; k += 4)
+                        *reinterpret_cast<float4*>(prow + col + k) =
+                            make_float4(acc[c][k], acc[c][k + 1], acc[c][k + 2], acc[c][k + 3]);
+                }
+            }
+        }
+    } else if constexpr (kWideComb) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) comb[team * HT + (c * TEAM + lt) * VEC + k] = acc[c][k];
+        }
+        __syncthreads();
+        for (int col = tid; col < H && col < HT; col += WG) {
+            float sum = comb[col];
+            for (int t = 1; t < R; ++t) sum += comb[t * HT + col];
+            prow[col] = sum;
+        }
+    } else {
+        for (int t = 0; t < R; ++t) {
+            if (team == t) {
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) {
+                        const int col = (c * TEAM + lt) * VEC + k;
+                        comb[col] = (t == 0) ? acc[c][k] : comb[col] + acc[c][k];
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        for (int col = tid; col < H && col < HT; col += WG) prow[col] = comb[col];
+    }
+}
+
+// dw[j] = sum_{g < G} partial[g][j], fixed order: 16 strided partial sums per
+// column (g = gl, gl + 16, ...), then added in gl order.
+template <typename T>
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict__ partial, int G,
+                                                        int ldp, int H, T* __restrict__ dw) {
+    __shared__ float part[16][64];
+    const int cl = threadIdx.x % 16;
+    const int gl = threadIdx.x / 16;
+    const int col0 = blockIdx.x * 64 + cl * 4;  // ldp is a multiple of 64: col0 + 3 < ldp
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int g = gl; g < G; g += 16) {
+        const float4 p = *reinterpret_cast<const float4*>(partial + (int64_t)g * ldp + col0);
+        a0 += p.x; a1 += p.y; a2 += p.z; a3 += p.w;
+    }
+    part[gl][cl * 4 + 0] = a0;
+    part[gl][cl * 4 + 1] = a1;
+    part[gl][cl * 4 + 2] = a2;
+    part[gl][cl * 4 + 3] = a3;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int col = blockIdx.x * 64 + threadIdx.x;
+        float s = part[0][threadIdx.x];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) s += part[j][threadIdx.x];
+        if (col < H) {
+            float o[1] = {s};
+            store_vec<T, 1>(dw + col, o);
+        }
+    }
+}
+
+#ifndef RMS_BWD_MAX_GROUPS
+#define RMS_BWD_MAX_GROUPS 256
+#endif
+#ifndef RMS_BWD_MIN_ROWS_PER_GROUP
+#define RMS_BWD_MIN_ROWS_PER_GROUP 4
+#endif
+
+int bwd_groups(int64_t rows, int64_t H, DType dt) {
+    (void)H; (void)dt;
+    if (rows <= 0) return 0;
+    int64_t g = (rows + RMS_BWD_MIN_ROWS_PER_GROUP - 1) / RMS_BWD_MIN_ROWS_PER_GROUP;
+    return (int)(g < RMS_BWD_MAX_GROUPS ? g : RMS_BWD_MAX_GROUPS);
+}
+
+int partial_ld(int64_t H) { return (int)((H + 63) / 64 * 64); }
+
+template <typename T, int VEC, int TEAM, int NCH>
+static hipError_t launch_rows_cfg(const BwdArgs& a, hipStream_t s) {
+    // Workgroup size by elements per lane (E): small tiles share 1024-lane
+    // workgroups among several rows, larger tiles use smaller workgroups so
+    // that the row, its prefetched successor, w and the dw sums stay in
+    // registers.  Teams wider than that fill the workgroup alone.
+    constexpr int E = NCH * VEC;
+    constexpr int WGD = E <= 8 ? 1024 : (E <= 16 ? 512 : 256);
+    constexpr int WG = TEAM > WGD ? TEAM : WGD;
+    const int64_t rpg = (a.rows + a.G - 1) / a.G;
+    if (a.dres) {
+        hipLaunchKernelGGL((bwd_rows_kernel<T, VEC, TEAM, NCH, WG, true>), dim3(a.G), dim3(WG), 0,
+                           s, (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
+                           (const T*)a.dres, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, rpg, a.eps);
+    } else {
+        hipLaunchKernelGGL((bwd_rows_kernel<T, VEC, TEAM, NCH, WG, false>), dim3(a.G), dim3(WG), 0,
+                           s, (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
+                           (const T*)nullptr, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, rpg, a.eps);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int VEC>
+static hipError_t dispatch_rows(const BwdArgs& a, hipStream_t s) {
+    Geometry g;
+    if (!choose_geometry(a.H, VEC, &g)) return hipErrorInvalidValue;
+#define RMS_CASE(TM, NC) \
+    if (g.team == TM && g.nch == NC) return launch_rows_cfg<T, VEC, TM, NC>(a, s);
+    RMS_CASE(1, 1) RMS_CASE(2, 1) RMS_CASE(4, 1) RMS_CASE(8, 1) RMS_CASE(16, 1) RMS_CASE(32, 1)
+    RMS_CASE(64, 1) RMS_CASE(64, 2) RMS_CASE(128, 2) RMS_CASE(256, 2) RMS_CASE(512, 2)
+    RMS_CASE(1024, 2) RMS_CASE(1024, 4) RMS_CASE(1024, 8) RMS_CASE(1024, 16)
+#undef RMS_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_rows(DType dt, int vec, const BwdArgs& a, hipStream_t s) {
+    if (dt == DType::F32) {
+        return vec == 4 ? dispatch_rows<float, 4>(a, s) : dispatch_rows<float, 1>(a, s);
+    }
+    return vec == 8 ? dispatch_rows<bf16_t, 8>(a, s) : dispatch_rows<bf16_t, 1>(a, s);
+}
+
+hipError_t launch_dw_reduce(DType dt, const float* partial, int G, int ldp, int H, void* dw,
+                            hipStream_t s) {
+    const int grid = ldp / 64;
+    if (dt == DType::F32) {
+        hipLaunchKernelGGL((dw_reduce_kernel<float>), dim3(grid), dim3(256), 0, s, partial, G, ldp, H,
+                           (float*)dw);
+    } else {
+        hipLaunchKernelGGL((dw_reduce_kernel<bf16_t>), dim3(grid), dim3(256), 0, s, partial, G, ldp,
+                           H, (bf16_t*)dw);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace rms

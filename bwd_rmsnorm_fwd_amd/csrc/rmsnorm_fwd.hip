@@ -1,0 +1,164 @@
+// Forward RMSNorm and residual-add + RMSNorm row kernels for gfx950.
+//
+// P1 = "训推加速 Qwen3 实战：从“调包”到手写 Triton Kernel（含 backward）":
+//   §4.1 y = w * x / sqrt(mean(x^2) + eps) per row; §4.2 one program per row,
+//   fp32 upcast, masked tail contributing zero, mean over the true width.
+// P2 = trdm.cn/news/483216 (hand-written Triton decode kernels): §2.1 the
+//   residual_add -> rms_norm pair and the fused kernel planned there.
+//
+// Design (MI355X): a team of TEAM lanes owns a row (several rows per
+// wavefront for narrow H, a whole workgroup for wide H); the row stays in
+// registers between the sum of squares and the scaled store, so x is read
+// from HBM exactly once.  Loads/stores are 128-bit per lane and contiguous
+// across the team.  The sum of squares is exact-product fp32 accumulated in
+// fp64 per lane, reduced with DPP inside 16-lane rows and lane reads across
+// rows (LDS across wavefronts).  Workgroups are persistent up to a grid cap
+// and prefetch their next row while finishing the current one.
+#include "common.hpp"
+#include "launch.hpp"
+
+#ifndef RMS_FWD_MAX_GRID
+#define RMS_FWD_MAX_GRID (256 * 16)
+#endif
+
+namespace rms {
+
+template <typename T, int VEC, int TEAM, int NCH, int WG, bool RES>
+__global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const T* __restrict__ w,
+                                                 T* h, T* __restrict__ y,
+                                                 float* __restrict__ rstd, int64_t rows, int H,
+                                                 float eps) {
+    constexpr int R = WG / TEAM;  // rows per workgroup iteration
+    constexpr int NWT = TEAM > kWave ? TEAM / kWave : 1;
+    // Register budget: keep w and a prefetched row in registers unless the
+    // per-lane tile is large for this workgroup size.
+    constexpr int E = NCH * VEC;
+    constexpr bool kCacheW = E * WG <= 32768;
+    constexpr bool kPrefetch = E * WG <= 32768;
+    __shared__ double red[TEAM > kWave ? R * NWT : 1];
+
+    const int tid = threadIdx.x;
+    const int team = tid / TEAM;
+    const int lt = tid % TEAM;
+    const int64_t nrb = (rows + R - 1) / R;
+
+    float wv[kCacheW ? NCH : 1][VEC];
+    if constexpr (kCacheW) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int col = (c * TEAM + lt) * VEC;
+            Pack<T, VEC> p = col < H ? load_pack<T, VEC>(w + col) : zero_pack<T, VEC>();
+            unpack(p, wv[c]);
+        }
+    }
+
+    struct RowRegs {
+        Pack<T, VEC> x[NCH], r[RES ? NCH : 1];
+    };
+    auto load_row = [&](int64_t rb, RowRegs& q) {
+        const int64_t row = rb * R + team;
+        const bool active = row < rows;
+        const int64_t off = row * (int64_t)H;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int col = (c * TEAM + lt) * VEC;
+            const bool ok = active && col < H;
+            q.x[c] = ok ? load_pack<T, VEC>(x + off + col) : zero_pack<T, VEC>();
+            if constexpr (RES) q.r[c] = ok ? load_pack<T, VEC>(res + off + col) : zero_pack<T, VEC>();
+        }
+    };
+
+    RowRegs cur;
+    int64_t rb = blockIdx.x;
+    if (kPrefetch && rb < nrb) load_row(rb, cur);
+    while (rb < nrb) {
+        const int64_t nb = rb + gridDim.x;
+        RowRegs nxt;
+        if constexpr (kPrefetch) {
+            if (nb < nrb) load_row(nb, nxt);
+        } else {
+            load_row(rb, cur);
+        }
+
+        const int64_t row = rb * R + team;
+        const bool active = row < rows;
+        const int64_t off = row * (int64_t)H;
+        float v[NCH][VEC];
+        double ss = 0.0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            unpack(cur.x[c], v[c]);
+            if constexpr (RES) {
+                float rv[VEC];
+                unpack(cur.r[c], rv);
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) v[c][k] = round_to(v[c][k] + rv[k], (T*)nullptr);
+                const int col = (c * TEAM + lt) * VEC;
+                if (active && col < H) store_vec<T, VEC>(h + off + col, v[c]);
+            }
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) ss += sq64(v[c][k], (T*)nullptr);
+        }
+        ss = team_sum<TEAM>(ss, red);
+        const double r = 1.0 / sqrt(ss / (double)H + (double)eps);
+        const float rf = (float)r;
+        if (active && lt == 0 && rstd) rstd[row] = rf;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int col = (c * TEAM + lt) * VEC;
+            float wc[VEC], o[VEC];
+            if constexpr (kCacheW) {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) wc[k] = wv[c][k];
+            } else {
+                unpack(col < H ? load_pack<T, VEC>(w + col) : zero_pack<T, VEC>(), wc);
+            }
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) o[k] = (v[c][k] * rf) * wc[k];
+            if (active && col < H) store_vec<T, VEC>(y + off + col, o);
+        }
+
+        if constexpr (kPrefetch) cur = nxt;
+        rb = nb;
+    }
+}
+
+template <typename T, int VEC, int TEAM, int NCH>
+static hipError_t launch_cfg(const FwdArgs& a, bool residual, hipStream_t s) {
+    constexpr int WG = TEAM > 256 ? TEAM : 256;
+    constexpr int R = WG / TEAM;
+    const int64_t nrb = (a.rows + R - 1) / R;
+    const int grid = (int)(nrb < RMS_FWD_MAX_GRID ? nrb : RMS_FWD_MAX_GRID);
+    if (residual) {
+        hipLaunchKernelGGL((fwd_kernel<T, VEC, TEAM, NCH, WG, true>), dim3(grid), dim3(WG), 0, s,
+                           (const T*)a.x, (const T*)a.res, (const T*)a.w, (T*)a.h, (T*)a.y, a.rstd,
+                           a.rows, a.H, a.eps);
+    } else {
+        hipLaunchKernelGGL((fwd_kernel<T, VEC, TEAM, NCH, WG, false>), dim3(grid), dim3(WG), 0, s,
+                           (const T*)a.x, (const T*)nullptr, (const T*)a.w, (T*)nullptr, (T*)a.y,
+                           a.rstd, a.rows, a.H, a.eps);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int VEC>
+static hipError_t dispatch(const FwdArgs& a, bool residual, hipStream_t s) {
+    Geometry g;
+    if (!choose_geometry(a.H, VEC, &g)) return hipErrorInvalidValue;
+#define RMS_CASE(TM, NC) \
+    if (g.team == TM && g.nch == NC) return launch_cfg<T, VEC, TM, NC>(a, residual, s);
+    RMS_CASE(1, 1) RMS_CASE(2, 1) RMS_CASE(4, 1) RMS_CASE(8, 1) RMS_CASE(16, 1) RMS_CASE(32, 1)
+    RMS_CASE(64, 1) RMS_CASE(64, 2) RMS_CASE(128, 2) RMS_CASE(256, 2) RMS_CASE(512, 2)
+    RMS_CASE(1024, 2) RMS_CASE(1024, 4) RMS_CASE(1024, 8) RMS_CASE(1024, 16)
+#undef RMS_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd(DType dt, int vec, const FwdArgs& a, bool residual, hipStream_t s) {
+    if (dt == DType::F32) {
+        return vec == 4 ? dispatch<float, 4>(a, residual, s) : dispatch<float, 1>(a, residual, s);
+    }
+    return vec == 8 ? dispatch<bf16_t, 8>(a, residual, s) : dispatch<bf16_t, 1>(a, residual, s);
+}
+
+}  // namespace rms

@@ -1,0 +1,146 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/*.h declares, and rejects bad arguments before touching the device.
+Only validation paths are called here (no kernel is launched)."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+from bwd_rmsnorm_fwd_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(rmsnorm_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for fn in ("rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_residual_fwd", "rmsnorm_fwd_splitrow",
+               "rmsnorm_bwd_workspace_bytes", "rmsnorm_status_str"):
+        assert fn in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for fn in declared_functions():
+        assert hasattr(L, fn), f"{fn} declared in include/ but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (rmsnorm_\w+)", out))
+    assert set(declared_functions()) == exported, exported ^ set(declared_functions())
+
+
+def test_header_compiles_as_c():
+    """The header is plain C (extern "C" guarded) and compiles alone."""
+    src = '#include "rmsnorm.h"\nint main(void){return (int)RMSNORM_OK;}\n'
+    r = subprocess.run(["gcc", "-x", "c", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-"],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings():
+    for code in range(6):
+        assert B.status_str(code)
+    assert B.status_str(99) == "unknown status"
+
+
+def _fwd(*a):
+    return B.lib().rmsnorm_fwd(*a)
+
+
+MIS = ctypes.c_void_p(0x1001)  # misaligned pseudo-pointer: rejected before any launch
+
+
+def test_fwd_validation():
+    nul = None
+    stream = None
+    assert _fwd(nul, nul, nul, nul, 4, 64, 1e-6, B.BF16, stream) == B.EINVAL       # null pointers
+    assert _fwd(MIS, MIS, MIS, nul, 4, 64, 1e-6, 7, stream) == B.EINVAL            # bad dtype
+    assert _fwd(MIS, MIS, MIS, nul, -1, 64, 1e-6, B.BF16, stream) == B.EINVAL      # rows < 0
+    assert _fwd(MIS, MIS, MIS, nul, 4, 0, 1e-6, B.BF16, stream) == B.EINVAL        # H < 1
+    assert _fwd(MIS, MIS, MIS, nul, 4, 64, -1e-6, B.BF16, stream) == B.EINVAL      # eps < 0
+    assert _fwd(MIS, MIS, MIS, nul, 4, 64, float("nan"), B.BF16, stream) == B.EINVAL
+    assert _fwd(MIS, MIS, MIS, nul, 4, 64, float("inf"), B.BF16, stream) == B.EINVAL
+    assert _fwd(MIS, MIS, MIS, nul, 4, B.MAX_H + 1, 1e-6, B.BF16, stream) == B.EUNSUPPORTED
+    assert _fwd(MIS, MIS, MIS, nul, 4, 64, 1e-6, B.BF16, stream) == B.EALIGN       # odd address
+    assert _fwd(MIS, MIS, MIS, nul, 0, 64, 1e-6, B.BF16, stream) == B.OK           # rows = 0: no-op
+
+
+def test_bwd_validation_and_workspace():
+    L = B.lib()
+    need = L.rmsnorm_bwd_workspace_bytes(4096, 4096, B.BF16)
+    assert need > 0 and need % 16 == 0
+    assert L.rmsnorm_bwd_workspace_bytes(0, 4096, B.BF16) == 0
+    assert L.rmsnorm_bwd_workspace_bytes(-1, 4096, B.BF16) == 0
+    assert L.rmsnorm_bwd_workspace_bytes(10, 0, B.BF16) == 0
+    A = ctypes.c_void_p(0x10000)  # aligned pseudo-pointer, never dereferenced here
+    # Workspace too small is caught before any launch.
+    st = L.rmsnorm_bwd(A, A, A, None, None, A, A, A, need - 1, 4096, 4096, 1e-6, B.BF16, None)
+    assert st == B.EWORKSPACE
+    st = L.rmsnorm_bwd(A, A, A, None, None, A, A, None, 0, 4096, 4096, 1e-6, B.BF16, None)
+    assert st == B.EWORKSPACE
+    st = L.rmsnorm_bwd(A, A, A, None, None, A, None, A, need, 4096, 4096, 1e-6, B.BF16, None)
+    assert st == B.EINVAL                                                   # dw missing
+    st = L.rmsnorm_bwd(A, None, A, None, None, A, A, A, need, 4096, 4096, 1e-6, B.BF16, None)
+    assert st == B.EINVAL                                                   # x missing
+    st = L.rmsnorm_bwd(A, A, A, None, MIS, A, A, A, need, 4096, 4096, 1e-6, B.BF16, None)
+    assert st == B.EALIGN                                                   # misaligned dres
+    st = L.rmsnorm_bwd_rows(A, A, A, None, None, A, A, need, 0, 4096, 1e-6, B.BF16, None)
+    assert st == B.EINVAL                                                   # rows pass needs rows
+    # Workspace size is a pure function of the shape: monotone in rows, capped.
+    sizes = [L.rmsnorm_bwd_workspace_bytes(r, 4096, B.BF16) for r in (1, 8, 64, 1024, 1 << 20)]
+    assert sizes == sorted(sizes) and sizes[-1] == sizes[-2]
+
+
+def test_splitrow_validation():
+    L = B.lib()
+    A = ctypes.c_void_p(0x10000)
+    assert L.rmsnorm_splitrow_partials_count(1, 4) == 4
+    assert L.rmsnorm_splitrow_partials_count(3, 16) == 48
+    assert L.rmsnorm_splitrow_partials_count(1, 0) == 0
+    assert L.rmsnorm_splitrow_partials_count(1, B.MAX_SPLITS + 1) == 0
+    f = L.rmsnorm_fwd_splitrow
+    assert f(A, A, A, None, A, 4, 1, 896, 1e-6, 0, B.BF16, None) == B.EINVAL        # splits = 0
+    assert f(A, A, A, None, A, 4, 1, 896, 1e-6, 65, B.BF16, None) == B.EINVAL       # > max
+    assert f(A, A, A, None, A, 3, 1, 896, 1e-6, 4, B.BF16, None) == B.EWORKSPACE    # too few
+    assert f(A, A, A, None, None, 4, 1, 896, 1e-6, 4, B.BF16, None) == B.EWORKSPACE
+    assert f(A, A, A, None, A, 4, 0, 896, 1e-6, 4, B.BF16, None) == B.EINVAL        # rows = 0
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The Python binding refuses host tensors and wrong sizes before any call."""
+    import torch
+    x = torch.zeros((4, 8), dtype=torch.bfloat16)
+    w = torch.zeros(8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        B.rmsnorm_fwd(x, w, x.clone(), None)      # host tensors are refused
+
+
+def test_bench_refuses_multi_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_bench_byte_formulas():
+    sys.path.insert(0, ROOT)
+    import bench
+    # rows * (2 H e + 4) + H e for the forward of the bf16 4096 x 4096 workload.
+    assert bench.fwd_bytes(4096, 4096, 2) == 67_133_440
+    assert bench.bwd_bytes(4096, 4096, 2) == 100_696_064
+    assert bench.fwd_bytes(16384, 4096, 2, residual=True) == 536_944_640
+    assert bench.bwd_bytes(16384, 4096, 2, dres=True) == 536_952_832
+    assert bench.fwd_bytes(262144, 128, 2) == 135_266_560
+    assert bench.bwd_bytes(8192, 8192, 2) == 402_718_720
+    assert bench.fwd_bytes(64, 896, 4) == 462_592

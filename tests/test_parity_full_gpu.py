@@ -1,0 +1,116 @@
+"""GPU parity at the workloads' full sizes, through the same entry points and
+launch configuration the benchmark times, against the double-precision
+oracle on every element (the C oracle runs these sizes in seconds).
+
+Workloads (synthetic, seeded; see bwd_rmsnorm_fwd_amd/synth.py):
+  c1 fp32 64x896, c2 bf16 4096x4096 with outlier feature columns,
+  c3 bf16 decode 1x896 (split-row with 4/8/16 splits and unsplit),
+  c4 bf16 residual 16384x4096 (+ its backward with dres),
+  c5a bf16 262144x128, c5b bf16 8192x8192.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bwd_rmsnorm_fwd_amd import binding as B
+from bwd_rmsnorm_fwd_amd import synth
+from _gpu_util import (DEV, assert_dw, assert_output, assert_rstd, f64, round_f32, to_dev,
+                       torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+TRAIN = ["c1_f32_64x896", "c2_bf16_4096x4096", "c5a_bf16_262144x128", "c5b_bf16_8192x8192"]
+
+
+def _ws(rows, H, dtype):
+    code = B.F32 if dtype == synth.F32 else B.BF16
+    return torch.empty(max(B.rmsnorm_bwd_workspace_bytes(rows, H, code), 16), dtype=torch.uint8,
+                       device=DEV)
+
+
+@pytest.mark.parametrize("name", TRAIN)
+def test_workload_fwd_bwd(name):
+    wl = synth.WORKLOADS[name]
+    rows, H, dt = wl.rows, wl.H, wl.dtype
+    print(f"[full] {name}: rows={rows} H={H} dtype={dt}", flush=True)
+    x, w, dy = wl.x(), wl.w(), wl.dy()
+    xd, wd, dyd = to_dev(x, dt), to_dev(w, dt), to_dev(dy, dt)
+    td = torch_dtype(dt)
+    y = torch.empty((rows, H), dtype=td, device=DEV)
+    rstd = torch.empty(rows, device=DEV)
+    dx = torch.empty((rows, H), dtype=td, device=DEV)
+    dw = torch.empty(H, dtype=td, device=DEV)
+    ws = _ws(rows, H, dt)
+    B.rmsnorm_fwd(xd, wd, y, rstd, wl.eps)
+    B.rmsnorm_bwd_rows(dyd, xd, wd, rstd, None, dx, ws, wl.eps)
+    B.rmsnorm_bwd_dw_reduce(ws, dw, rows)
+    torch.cuda.synchronize()
+    x64, w64, dy64 = (synth.to_f64(a, dt) for a in (x, w, dy))
+    del x, dy
+    yo, ro = oracle.rmsnorm_fwd(x64, w64, wl.eps)
+    e_y = assert_output("y", f64(y), yo, dt)
+    del yo
+    e_r = assert_rstd(f64(rstd), ro)
+    rs = f64(rstd)
+    # Backward against the oracle given the same stored fp32 statistic; the
+    # statistic itself is the fp32 rounding of the oracle's r.
+    n_tie = int(np.sum(rs != round_f32(ro)))
+    assert n_tie <= max(1, rows // 100000), f"{n_tie} rows with rstd != rounded r"
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=rs)
+    e_dx = assert_output("dx", f64(dx), dxo, dt)
+    e_dw = assert_dw(f64(dw), dwo, dt)
+    print(f"[full] {name}: y {e_y:.3g}  rstd {e_r:.3g}  dx {e_dx:.3g}  dw {e_dw:.3g}  "
+          f"rstd!=round(r): {n_tie}", flush=True)
+
+
+def test_workload_residual_fwd_bwd():
+    wl = synth.WORKLOADS["c4_bf16_residual_16384x4096"]
+    rows, H, dt = wl.rows, wl.H, wl.dtype
+    print(f"[full] {wl.name}: rows={rows} H={H}", flush=True)
+    x, res, w, dy, dres = wl.x(), wl.res(), wl.w(), wl.dy(), wl.dres()
+    xd, rd, wd, dyd, drd = (to_dev(a, dt) for a in (x, res, w, dy, dres))
+    td = torch_dtype(dt)
+    h = torch.empty((rows, H), dtype=td, device=DEV)
+    y = torch.empty((rows, H), dtype=td, device=DEV)
+    rstd = torch.empty(rows, device=DEV)
+    dh = torch.empty((rows, H), dtype=td, device=DEV)
+    dw = torch.empty(H, dtype=td, device=DEV)
+    B.rmsnorm_residual_fwd(xd, rd, wd, h, y, rstd, wl.eps)
+    B.rmsnorm_bwd(dyd, h, wd, rstd, drd, dh, dw, _ws(rows, H, dt), wl.eps)
+    torch.cuda.synchronize()
+    del xd, rd
+    ho, yo, ro = oracle.rmsnorm_residual_fwd(synth.to_f64(x, dt), synth.to_f64(res, dt),
+                                             synth.to_f64(w, dt), wl.eps, oracle.H_BF16)
+    del x, res
+    assert np.array_equal(f64(h), ho), "h must be bit-exact"
+    e_y = assert_output("y", f64(y), yo, dt)
+    del yo
+    e_r = assert_rstd(f64(rstd), ro)
+    dho, dwo = oracle.rmsnorm_bwd(synth.to_f64(dy, dt), ho, synth.to_f64(w, dt), wl.eps,
+                                  rstd=f64(rstd), dres=synth.to_f64(dres, dt))
+    e_dh = assert_output("dh", f64(dh), dho, dt)
+    e_dw = assert_dw(f64(dw), dwo, dt)
+    print(f"[full] {wl.name}: y {e_y:.3g}  rstd {e_r:.3g}  dh {e_dh:.3g}  dw {e_dw:.3g}",
+          flush=True)
+
+
+@pytest.mark.parametrize("splits", [1, 4, 8, 16])
+def test_workload_decode_splitrow(splits):
+    wl = synth.WORKLOADS["c3_bf16_decode_1x896"]
+    rows, H, dt = wl.rows, wl.H, wl.dtype
+    x, w = wl.x(), wl.w()
+    xd, wd = to_dev(x, dt), to_dev(w, dt)
+    y = torch.empty((rows, H), dtype=torch_dtype(dt), device=DEV)
+    rstd = torch.empty(rows, device=DEV)
+    partials = torch.full((B.rmsnorm_splitrow_partials_count(rows, splits) + 16,), float("nan"),
+                          device=DEV)
+    B.rmsnorm_fwd_splitrow(xd, wd, y, rstd, partials, splits, wl.eps)
+    y_plain = torch.empty_like(y)
+    B.rmsnorm_fwd(xd, wd, y_plain, None, wl.eps)
+    torch.cuda.synchronize()
+    yo, ro = oracle.rmsnorm_fwd(synth.to_f64(x, dt), synth.to_f64(w, dt), wl.eps)
+    assert_output("y", f64(y), yo, dt)
+    assert_rstd(f64(rstd), ro)
+    # Split and unsplit agree to within one bf16 ulp of each other.
+    assert np.max(np.abs(f64(y) - f64(y_plain))) <= np.max(np.abs(yo)) * 2.0 ** -7

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP library (through the C ABI) against the double-precision
+oracle, element by element, on seeded inputs.
+
+Shapes span several tiles and ragged tails on both the 128-bit path and the
+scalar path (odd H, unaligned pointers), every team width of the dispatch
+table, and the degenerate cases (rows = 0, H = 1).  Full-size workloads are in
+test_parity_full_gpu.py.
+
+Tolerances: fp32 I/O 2e-6 normwise per tensor; bf16 I/O 1 bf16 ulp per element
+on y and dx, bit-exact h, 1e-2 normwise on dw; fp32 rstd 2e-6 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bwd_rmsnorm_fwd_amd import binding as B
+from bwd_rmsnorm_fwd_amd import synth
+from _gpu_util import (DEV, assert_dw, assert_output, assert_rstd, f64, round_f32, to_dev,
+                       torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+# (rows, H): tails of every team width, several tiles, vector and scalar paths.
+SHAPES = [(1, 1), (3, 2), (5, 7), (64, 8), (65, 16), (33, 120), (257, 128), (17, 129),
+          (9, 256), (7, 500), (70, 512), (11, 895), (64, 896), (5, 897), (6, 1024),
+          (4, 2040), (3, 2048), (5, 4095), (7, 4096), (3, 5000), (2, 8192), (2, 16384)]
+DTYPES = [synth.BF16, synth.F32]
+
+
+def _inputs(rows, H, dtype, seed, outliers=0.0):
+    wl = synth.small_case(rows, H, dtype, seed=seed, outlier_frac=outliers)
+    return wl, wl.x(), wl.w(), wl.dy(), wl.res(), wl.dres()
+
+
+def _empty(rows, H, dtype):
+    return torch.full((rows, H), float("nan"), dtype=torch_dtype(dtype), device=DEV)
+
+
+def _ws(rows, H, dtype):
+    code = B.F32 if dtype == synth.F32 else B.BF16
+    n = B.rmsnorm_bwd_workspace_bytes(rows, H, code)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("rows,H", SHAPES)
+def test_fwd(rows, H, dtype):
+    wl, x, w, *_ = _inputs(rows, H, dtype, seed=rows * 7 + H, outliers=0.01)
+    xd, wd = to_dev(x, dtype), to_dev(w, dtype)
+    y = _empty(rows, H, dtype)
+    rstd = torch.full((rows,), float("nan"), device=DEV)
+    B.rmsnorm_fwd(xd, wd, y, rstd, wl.eps)
+    torch.cuda.synchronize()
+    yo, ro = oracle.rmsnorm_fwd(synth.to_f64(x, dtype), synth.to_f64(w, dtype), wl.eps)
+    assert_output("y", f64(y), yo, dtype)
+    assert_rstd(f64(rstd), ro)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("rows,H", SHAPES[::2])
+def test_residual_fwd(rows, H, dtype):
+    wl, x, w, _, res, _ = _inputs(rows, H, dtype, seed=rows + 3 * H)
+    xd, rd, wd = to_dev(x, dtype), to_dev(res, dtype), to_dev(w, dtype)
+    h, y = _empty(rows, H, dtype), _empty(rows, H, dtype)
+    rstd = torch.full((rows,), float("nan"), device=DEV)
+    B.rmsnorm_residual_fwd(xd, rd, wd, h, y, rstd, wl.eps)
+    torch.cuda.synchronize()
+    kind = oracle.H_BF16 if dtype == synth.BF16 else oracle.H_F32
+    ho, yo, ro = oracle.rmsnorm_residual_fwd(synth.to_f64(x, dtype), synth.to_f64(res, dtype),
+                                             synth.to_f64(w, dtype), wl.eps, kind)
+    assert np.array_equal(f64(h), ho), "h must be bit-exact"
+    assert_output("y", f64(y), yo, dtype)
+    assert_rstd(f64(rstd), ro)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("mode", ["saved_rstd", "recompute", "dres"])
+@pytest.mark.parametrize("rows,H", SHAPES)
+def test_bwd(rows, H, dtype, mode):
+    """The backward with the saved statistic (fp32 rstd) as its input on both
+    sides, with r recomputed from x, and with a residual-stream gradient."""
+    wl, x, w, dy, _, dres = _inputs(rows, H, dtype, seed=5 * rows + H, outliers=0.01)
+    x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
+    _, r64 = oracle.rmsnorm_fwd(x64, w64, wl.eps)
+    rstd32 = round_f32(r64)                      # the stored statistic, from the oracle
+    xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
+    rstd_d = torch.from_numpy(rstd32.astype(np.float32)).to(DEV) if mode != "recompute" else None
+    dres_d = to_dev(dres, dtype) if mode == "dres" else None
+    dx = _empty(rows, H, dtype)
+    dw = torch.full((H,), float("nan"), dtype=torch_dtype(dtype), device=DEV)
+    B.rmsnorm_bwd(dyd, xd, wd, rstd_d, dres_d, dx, dw, _ws(rows, H, dtype), wl.eps)
+    torch.cuda.synchronize()
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps,
+                                  rstd=None if mode == "recompute" else rstd32,
+                                  dres=synth.to_f64(dres, dtype) if mode == "dres" else None)
+    assert_output("dx", f64(dx), dxo, dtype)
+    assert_dw(f64(dw), dwo, dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("rows,H", [(64, 896), (33, 4096), (300, 128), (9, 8192)])
+def test_chain_fwd_then_bwd(rows, H, dtype):
+    """GPU forward's rstd fed to the GPU backward, against the oracle with r
+    recomputed in double: rstd within 2e-6, then dx/dw to the same bars."""
+    wl, x, w, dy, *_ = _inputs(rows, H, dtype, seed=rows + H)
+    x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
+    xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
+    y, rstd = _empty(rows, H, dtype), torch.empty(rows, device=DEV)
+    B.rmsnorm_fwd(xd, wd, y, rstd, wl.eps)
+    dx = _empty(rows, H, dtype)
+    dw = torch.empty(H, dtype=torch_dtype(dtype), device=DEV)
+    B.rmsnorm_bwd(dyd, xd, wd, rstd, None, dx, dw, _ws(rows, H, dtype), wl.eps)
+    torch.cuda.synchronize()
+    yo, ro = oracle.rmsnorm_fwd(x64, w64, wl.eps)
+    assert_rstd(f64(rstd), ro)
+    # The GPU's rstd is the correctly rounded fp32 r except on rare exact ties;
+    # the backward with it matches the oracle given that same fp32 value.
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=f64(rstd))
+    assert_output("dx", f64(dx), dxo, dtype)
+    assert_dw(f64(dw), dwo, dtype)
+    assert np.array_equal(f64(rstd), round_f32(ro)), "rstd is not the rounded double r"
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("rows,H", [(1, 896), (3, 896), (2, 4096), (1, 7), (4, 100)])
+@pytest.mark.parametrize("splits", [1, 2, 4, 8, 16, 64])
+def test_splitrow(rows, H, dtype, splits):
+    wl, x, w, *_ = _inputs(rows, H, dtype, seed=11 * H + rows)
+    xd, wd = to_dev(x, dtype), to_dev(w, dtype)
+    y = _empty(rows, H, dtype)
+    rstd = torch.empty(rows, device=DEV)
+    n = B.rmsnorm_splitrow_partials_count(rows, splits)
+    # The partial buffer is larger than needed and poisoned: the merge must
+    # read only its own `splits` entries per row.
+    partials = torch.full((n + 64,), float("nan"), device=DEV)
+    B.rmsnorm_fwd_splitrow(xd, wd, y, rstd, partials, splits, wl.eps)
+    torch.cuda.synchronize()
+    yo, ro = oracle.rmsnorm_fwd(synth.to_f64(x, dtype), synth.to_f64(w, dtype), wl.eps)
+    assert_output("y", f64(y), yo, dtype)
+    assert_rstd(f64(rstd), ro)
+    assert torch.isnan(partials[n:]).all()
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_unaligned_pointers_use_scalar_path(dtype):
+    """Row pointers off the 16-byte grid (one-element offset views)."""
+    rows, H = 37, 1024
+    wl, x, w, dy, *_ = _inputs(rows, H, dtype, seed=99)
+    td = torch_dtype(dtype)
+
+    def off(a):
+        t = to_dev(a.reshape(-1), dtype)
+        buf = torch.empty(t.numel() + 1, dtype=td, device=DEV)
+        buf[1:].copy_(t)
+        return buf[1:].view(a.shape)
+
+    xd, wd, dyd = off(x), off(w), off(dy)
+    ybuf = torch.full((rows * H + 1,), float("nan"), dtype=td, device=DEV)
+    y = ybuf[1:].view(rows, H)
+    rstd = torch.empty(rows, device=DEV)
+    B.rmsnorm_fwd(xd, wd, y, rstd, wl.eps)
+    dxbuf = torch.full((rows * H + 1,), float("nan"), dtype=td, device=DEV)
+    dx = dxbuf[1:].view(rows, H)
+    dw = torch.empty(H, dtype=td, device=DEV)
+    B.rmsnorm_bwd(dyd, xd, wd, rstd, None, dx, dw, _ws(rows, H, dtype), wl.eps)
+    torch.cuda.synchronize()
+    x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
+    yo, ro = oracle.rmsnorm_fwd(x64, w64, wl.eps)
+    assert_output("y", f64(y), yo, dtype)
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=f64(rstd))
+    assert_output("dx", f64(dx), dxo, dtype)
+    assert_dw(f64(dw), dwo, dtype)
+    assert torch.isnan(ybuf[0]) and torch.isnan(dxbuf[0])
+
+
+def test_rows_zero():
+    H = 256
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(H, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    B.rmsnorm_fwd(x, w, y, None, 1e-6)
+    dw = torch.full((H,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    B.rmsnorm_bwd(x, x, w, None, None, y, dw, None, 1e-6)
+    torch.cuda.synchronize()
+    assert (dw == 0).all()
+
+
+def test_guard_bands_untouched():
+    """Outputs sit between sentinel bands; the kernels write every output
+    element and nothing outside."""
+    rows, H, dtype = 129, 896, synth.BF16
+    wl, x, w, dy, res, dres = _inputs(rows, H, dtype, seed=3)
+    G = 4096
+    td = torch.bfloat16
+
+    def banded(n):
+        buf = torch.full((n + 2 * G,), 12345.0, dtype=td, device=DEV)
+        buf[G:G + n] = float("nan")
+        return buf, buf[G:G + n]
+
+    xd, wd, dyd, rd, drd = (to_dev(a, dtype) for a in (x, w, dy, res, dres))
+    hb, h = banded(rows * H)
+    yb, y = banded(rows * H)
+    dxb, dx = banded(rows * H)
+    dwb, dw = banded(H)
+    rb = torch.full((rows + 2 * G,), 777.0, device=DEV)
+    rstd = rb[G:G + rows]
+    B.rmsnorm_residual_fwd(xd, rd, wd, h.view(rows, H), y.view(rows, H), rstd, wl.eps)
+    B.rmsnorm_bwd(dyd, h.view(rows, H), wd, rstd, drd, dx.view(rows, H), dw, _ws(rows, H, dtype),
+                  wl.eps)
+    torch.cuda.synchronize()
+    for buf, n in ((hb, rows * H), (yb, rows * H), (dxb, rows * H), (dwb, H)):
+        assert (buf[:G] == 12345.0).all() and (buf[G + n:] == 12345.0).all()
+        assert not torch.isnan(buf[G:G + n]).any()
+    assert (rb[:G] == 777.0).all() and (rb[G + rows:] == 777.0).all()
+    assert not torch.isnan(rstd).any()
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_deterministic(dtype):
+    """Fixed reduction order: repeated calls give bitwise-identical results."""
+    rows, H = 1000, 4096
+    wl, x, w, dy, *_ = _inputs(rows, H, dtype, seed=1)
+    xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
+    outs = []
+    for _ in range(3):
+        y, rstd = _empty(rows, H, dtype), torch.empty(rows, device=DEV)
+        dx, dw = _empty(rows, H, dtype), torch.empty(H, dtype=torch_dtype(dtype), device=DEV)
+        B.rmsnorm_fwd(xd, wd, y, rstd, wl.eps)
+        B.rmsnorm_bwd(dyd, xd, wd, rstd, None, dx, dw, _ws(rows, H, dtype), wl.eps)
+        torch.cuda.synchronize()
+        outs.append([t.view(torch.int16 if t.element_size() == 2 else torch.int32).cpu()
+                     for t in (y, rstd, dx, dw)])
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a, b)
+
+
+def test_two_pass_api_equals_bwd():
+    rows, H, dtype = 300, 2048, synth.BF16
+    wl, x, w, dy, *_ = _inputs(rows, H, dtype, seed=8)
+    xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
+    dx1, dx2 = _empty(rows, H, dtype), _empty(rows, H, dtype)
+    dw1 = torch.empty(H, dtype=torch.bfloat16, device=DEV)
+    dw2 = torch.empty(H, dtype=torch.bfloat16, device=DEV)
+    ws = _ws(rows, H, dtype)
+    B.rmsnorm_bwd(dyd, xd, wd, None, None, dx1, dw1, ws, wl.eps)
+    B.rmsnorm_bwd_rows(dyd, xd, wd, None, None, dx2, ws, wl.eps)
+    B.rmsnorm_bwd_dw_reduce(ws, dw2, rows)
+    torch.cuda.synchronize()
+    assert torch.equal(dx1.view(torch.int16), dx2.view(torch.int16))
+    assert torch.equal(dw1.view(torch.int16), dw2.view(torch.int16))
+
+
+def test_errors_are_reported():
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(64, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty_like(x)
+    with pytest.raises(B.RMSNormError) as e:
+        B.rmsnorm_fwd(x, w, y, None, eps=-1.0)
+    assert e.value.status == B.EINVAL
+    ws = torch.empty(1, dtype=torch.uint8, device=DEV)
+    with pytest.raises(B.RMSNormError) as e:
+        B.rmsnorm_bwd(x, x, w, None, None, y, torch.empty(64, dtype=torch.bfloat16, device=DEV),
+                      ws, 1e-6)
+    assert e.value.status == B.EWORKSPACE
