@@ -17,8 +17,24 @@
 namespace rms {
 
 using bf16_t = uint16_t;  // storage of one bfloat16
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 128-bit access
 
 constexpr int kWave = 64;
+
+// 128-bit accesses.  NT = true marks a streaming access (each element is
+// touched once): a nontemporal load/store that does not keep the line in the
+// caches, which leaves them to the reused data (w, the dw partials).
+template <bool NT>
+__device__ __forceinline__ u32x4 ld128(const void* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st128(void* p, u32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = v;
+}
 
 // ---------------------------------------------------------------------------
 // Element I/O: VEC elements of T <-> VEC floats.
@@ -26,9 +42,9 @@ constexpr int kWave = 64;
 template <typename T, int VEC>
 struct Pack;  // raw storage of VEC elements
 
-template <> struct Pack<float, 4> { uint4 v; };
+template <> struct Pack<float, 4> { u32x4 v; };
 template <> struct Pack<float, 1> { float v; };
-template <> struct Pack<bf16_t, 8> { uint4 v; };
+template <> struct Pack<bf16_t, 8> { u32x4 v; };
 template <> struct Pack<bf16_t, 1> { bf16_t v; };
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -47,13 +63,14 @@ __device__ __forceinline__ float round_to(float v, bf16_t*) {
     return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v) << 16);
 }
 
-template <typename T, int VEC>
+template <typename T, int VEC, bool NT = false>
 __device__ __forceinline__ Pack<T, VEC> load_pack(const T* p) {
     Pack<T, VEC> r;
     if constexpr (VEC == 1) {
-        r.v = *p;
+        if constexpr (NT) r.v = __builtin_nontemporal_load(p);
+        else r.v = *p;
     } else {
-        r.v = *reinterpret_cast<const uint4*>(p);
+        r.v = ld128<NT>(p);
     }
     return r;
 }
@@ -64,7 +81,7 @@ __device__ __forceinline__ Pack<T, VEC> zero_pack() {
     if constexpr (VEC == 1) {
         r.v = 0;
     } else {
-        r.v = make_uint4(0, 0, 0, 0);
+        r.v = u32x4{0u, 0u, 0u, 0u};
     }
     return r;
 }
@@ -86,18 +103,21 @@ __device__ __forceinline__ void unpack(const Pack<T, VEC>& p, float (&f)[VEC]) {
     }
 }
 
-template <typename T, int VEC>
+template <typename T, int VEC, bool NT = false>
 __device__ __forceinline__ void store_vec(T* p, const float (&f)[VEC]) {
     if constexpr (sizeof(T) == 4 && VEC == 4) {
-        *reinterpret_cast<uint4*>(p) = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
-                                                  __float_as_uint(f[2]), __float_as_uint(f[3]));
+        st128<NT>(p, u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                       __float_as_uint(f[3])});
     } else if constexpr (sizeof(T) == 4 && VEC == 1) {
-        *reinterpret_cast<float*>(p) = f[0];
+        if constexpr (NT) __builtin_nontemporal_store(f[0], reinterpret_cast<float*>(p));
+        else *reinterpret_cast<float*>(p) = f[0];
     } else if constexpr (VEC == 8) {
-        *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                                                  pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+        st128<NT>(p, u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                       pack_bf16x2(f[6], f[7])});
     } else {
-        *p = __builtin_bit_cast(uint16_t, (__bf16)f[0]);
+        const uint16_t b = __builtin_bit_cast(uint16_t, (__bf16)f[0]);
+        if constexpr (NT) __builtin_nontemporal_store(b, p);
+        else *p = b;
     }
 }
 

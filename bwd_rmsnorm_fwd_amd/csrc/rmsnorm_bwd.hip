@@ -27,6 +27,26 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+// Streaming (nontemporal) access to the row tensors: dy/x/dres loads, dx
+// stores.  Measured best: loads only for the plain backward, loads and
+// stores with a residual-stream gradient.
+#ifndef RMS_BWD_NT_LOAD
+#define RMS_BWD_NT_LOAD 1
+#endif
+#ifndef RMS_BWD_NT_STORE
+#define RMS_BWD_NT_STORE 0
+#endif
+#ifndef RMS_DRES_NT_LOAD
+#define RMS_DRES_NT_LOAD 1
+#endif
+#ifndef RMS_DRES_NT_STORE
+#define RMS_DRES_NT_STORE 1
+#endif
+// Row blocks in flight per workgroup beyond the one being finished (1 or 2).
+#ifndef RMS_BWD_PREFETCH
+#define RMS_BWD_PREFETCH 1
+#endif
+
 namespace rms {
 
 template <typename T, int VEC, int TEAM, int NCH, int WG, bool DRES>
@@ -39,11 +59,14 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     constexpr int R = WG / TEAM;
     constexpr int NWT = TEAM > kWave ? TEAM / kWave : 1;
     constexpr int HT = TEAM * NCH * VEC;  // columns covered by one team
-    constexpr int E = NCH * VEC;          // elements per lane
+    constexpr int EB = NCH * VEC * (int)sizeof(T);  // bytes per lane per row tensor
     // Register budget: w cached and the next rows prefetched unless the
     // per-lane tile is large for this workgroup size.
-    constexpr bool kCacheW = E * WG <= 8192;
-    constexpr bool kPrefetch = E * WG <= 8192;
+    constexpr bool kCacheW = EB * WG <= 16384;
+    constexpr bool kPrefetch = EB * WG <= 16384;
+    constexpr bool kNtLoad = DRES ? RMS_DRES_NT_LOAD != 0 : RMS_BWD_NT_LOAD != 0;
+    constexpr bool kNtStore = DRES ? RMS_DRES_NT_STORE != 0 : RMS_BWD_NT_STORE != 0;
+    constexpr int kDepth = kPrefetch ? RMS_BWD_PREFETCH : 0;
     // Teams combine their dw sums either side by side ([R][HT], summed per
     // column in team order) when that fits in 32 KiB, or one after another
     // into a single [HT] row.
@@ -92,22 +115,30 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
         for (int c = 0; c < NCH; ++c) {
             const int col = (c * TEAM + lt) * VEC;
             const bool ok = active && col < H;
-            q.x[c] = ok ? load_pack<T, VEC>(x + off + col) : zero_pack<T, VEC>();
-            q.dy[c] = ok ? load_pack<T, VEC>(dy + off + col) : zero_pack<T, VEC>();
+            q.x[c] = ok ? load_pack<T, VEC, kNtLoad>(x + off + col) : zero_pack<T, VEC>();
+            q.dy[c] = ok ? load_pack<T, VEC, kNtLoad>(dy + off + col) : zero_pack<T, VEC>();
             if constexpr (DRES)
-                q.dr[c] = ok ? load_pack<T, VEC>(dres + off + col) : zero_pack<T, VEC>();
+                q.dr[c] = ok ? load_pack<T, VEC, kNtLoad>(dres + off + col) : zero_pack<T, VEC>();
         }
         q.rs = (active && has_rstd) ? rstd[row] : 0.f;
     };
 
+    // Ring of row blocks in flight: cur is being finished, ahead[d] is the
+    // block (d + 1) * R rows further on (loaded kDepth blocks ahead).
     RowRegs cur;
+    RowRegs ahead[kDepth > 0 ? kDepth : 1];
     int64_t base = begin;
-    if (kPrefetch && base < end) load_row(base, cur);
+    if constexpr (kDepth > 0) {
+        if (base < end) load_row(base, cur);
+#pragma unroll
+        for (int d = 0; d + 1 < kDepth; ++d)
+            if (base + (d + 1) * R < end) load_row(base + (d + 1) * R, ahead[d]);
+    }
     while (base < end) {
         const int64_t nb = base + R;
-        RowRegs nxt;
-        if constexpr (kPrefetch) {
-            if (nb < end) load_row(nb, nxt);
+        if constexpr (kDepth > 0) {
+            const int64_t fb = base + kDepth * R;
+            if (fb < end) load_row(fb, ahead[kDepth - 1]);
         } else {
             load_row(base, cur);
         }
@@ -148,19 +179,24 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
             unpack(cur.x[c], xv);
             unpack(cur.dy[c], dyv);
             weights(c, wc);
-            if constexpr (DRES) {
-                // dx and the residual-stream gradient can cancel; form
-                // r * (wdy - x k) + dres in fp64 and round once.
+            if constexpr (DRES || sizeof(T) == 4) {
+                // fp64 form: w*dy (exact in fp64), r*(wdy - x k) [+ dres] with
+                // one final rounding.  Used when dx can cancel against dres,
+                // and for fp32 inputs, whose w*dy is not exact in fp32.
                 float drv[VEC];
-                unpack(cur.dr[c], drv);
+                if constexpr (DRES) unpack(cur.dr[c], drv);
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) {
-                    const float wdy = wc[k] * dyv[k];
-                    const double t = __builtin_fma(-(double)xv[k], kk, (double)wdy);
-                    o[k] = (float)__builtin_fma(r, t, (double)drv[k]);
+                    const double wdy = (double)wc[k] * (double)dyv[k];
+                    const double t = __builtin_fma(-(double)xv[k], kk, wdy);
+                    if constexpr (DRES) o[k] = (float)__builtin_fma(r, t, (double)drv[k]);
+                    else o[k] = (float)(r * t);
                     acc[c][k] += (dyv[k] * xv[k]) * rf;
                 }
             } else {
+                // bf16 inputs: w*dy is exact in fp32, and two fused multiply-
+                // adds with k = k_hi + k_lo form wdy - x k to fp32 accuracy
+                // even where the two terms nearly cancel.
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) {
                     const float wdy = wc[k] * dyv[k];
@@ -171,10 +207,14 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
                 }
             }
             const int col = (c * TEAM + lt) * VEC;
-            if (active && col < H) store_vec<T, VEC>(dx + row * (int64_t)H + col, o);
+            if (active && col < H) store_vec<T, VEC, kNtStore>(dx + row * (int64_t)H + col, o);
         }
 
-        if constexpr (kPrefetch) cur = nxt;
+        if constexpr (kDepth > 0) {
+            cur = ahead[0];
+#pragma unroll
+            for (int d = 0; d + 1 < kDepth; ++d) ahead[d] = ahead[d + 1];
+        }
         base = nb;
     }
 
@@ -225,18 +265,36 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     }
 }
 
-// dw[j] = sum_{g < G} partial[g][j], fixed order: 16 strided partial sums per
-// column (g = gl, gl + 16, ...), then added in gl order.
+// dw[j] = sum_{g < G} partial[g][j] in a fixed order.  A workgroup owns
+// kRedCols columns (kRedCL lanes x 4 columns, 128-bit loads) and kRedGL lanes
+// over g: lane gl adds rows g = gl, gl + kRedGL, ... in increasing g (eight
+// independent loads in flight per step), then the kRedGL lane sums of each
+// column are added in gl order.
+constexpr int kRedCL = 8;
+constexpr int kRedGL = 256 / kRedCL;
+constexpr int kRedCols = 4 * kRedCL;
+
 template <typename T>
 __global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict__ partial, int G,
                                                         int ldp, int H, T* __restrict__ dw) {
-    __shared__ float part[16][64];
-    const int cl = threadIdx.x % 16;
-    const int gl = threadIdx.x / 16;
-    const int col0 = blockIdx.x * 64 + cl * 4;  // ldp is a multiple of 64: col0 + 3 < ldp
+    __shared__ float part[kRedGL][kRedCols + 1];
+    const int cl = threadIdx.x % kRedCL;
+    const int gl = threadIdx.x / kRedCL;
+    // ldp is a multiple of 64, so col0 + 3 < ldp for every workgroup.
+    const int col0 = blockIdx.x * kRedCols + cl * 4;
+    const float* base = partial + col0;
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int g = gl; g < G; g += 16) {
-        const float4 p = *reinterpret_cast<const float4*>(partial + (int64_t)g * ldp + col0);
+    int g = gl;
+    for (; g + 7 * kRedGL < G; g += 8 * kRedGL) {
+        float4 p[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            p[u] = *reinterpret_cast<const float4*>(base + (int64_t)(g + u * kRedGL) * ldp);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { a0 += p[u].x; a1 += p[u].y; a2 += p[u].z; a3 += p[u].w; }
+    }
+    for (; g < G; g += kRedGL) {
+        const float4 p = *reinterpret_cast<const float4*>(base + (int64_t)g * ldp);
         a0 += p.x; a1 += p.y; a2 += p.z; a3 += p.w;
     }
     part[gl][cl * 4 + 0] = a0;
@@ -244,13 +302,13 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict_
     part[gl][cl * 4 + 2] = a2;
     part[gl][cl * 4 + 3] = a3;
     __syncthreads();
-    if (threadIdx.x < 64) {
-        const int col = blockIdx.x * 64 + threadIdx.x;
-        float s = part[0][threadIdx.x];
+    if (threadIdx.x < kRedCols) {
+        const int col = blockIdx.x * kRedCols + threadIdx.x;
+        float sum = part[0][threadIdx.x];
 #pragma unroll
-        for (int j = 1; j < 16; ++j) s += part[j][threadIdx.x];
+        for (int j = 1; j < kRedGL; ++j) sum += part[j][threadIdx.x];
         if (col < H) {
-            float o[1] = {s};
+            float o[1] = {sum};
             store_vec<T, 1>(dw + col, o);
         }
     }
@@ -274,12 +332,12 @@ int partial_ld(int64_t H) { return (int)((H + 63) / 64 * 64); }
 
 template <typename T, int VEC, int TEAM, int NCH>
 static hipError_t launch_rows_cfg(const BwdArgs& a, hipStream_t s) {
-    // Workgroup size by elements per lane (E): small tiles share 1024-lane
+    // Workgroup size by bytes per lane (EB): small tiles share 1024-lane
     // workgroups among several rows, larger tiles use smaller workgroups so
     // that the row, its prefetched successor, w and the dw sums stay in
     // registers.  Teams wider than that fill the workgroup alone.
-    constexpr int E = NCH * VEC;
-    constexpr int WGD = E <= 8 ? 1024 : (E <= 16 ? 512 : 256);
+    constexpr int EB = NCH * VEC * (int)sizeof(T);
+    constexpr int WGD = EB <= 16 ? 1024 : (EB <= 32 ? 512 : 256);
     constexpr int WG = TEAM > WGD ? TEAM : WGD;
     const int64_t rpg = (a.rows + a.G - 1) / a.G;
     if (a.dres) {
@@ -316,7 +374,7 @@ hipError_t launch_bwd_rows(DType dt, int vec, const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_dw_reduce(DType dt, const float* partial, int G, int ldp, int H, void* dw,
                             hipStream_t s) {
-    const int grid = ldp / 64;
+    const int grid = ldp / kRedCols;
     if (dt == DType::F32) {
         hipLaunchKernelGGL((dw_reduce_kernel<float>), dim3(grid), dim3(256), 0, s, partial, G, ldp, H,
                            (float*)dw);

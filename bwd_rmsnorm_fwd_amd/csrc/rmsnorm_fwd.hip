@@ -20,6 +20,25 @@
 #ifndef RMS_FWD_MAX_GRID
 #define RMS_FWD_MAX_GRID (256 * 16)
 #endif
+// Streaming (nontemporal) access to the row tensors: x/res loads, y/h
+// stores.  Measured best: stores only for the plain forward, loads and
+// stores for the residual forward.
+#ifndef RMS_FWD_NT_LOAD
+#define RMS_FWD_NT_LOAD 0
+#endif
+#ifndef RMS_FWD_NT_STORE
+#define RMS_FWD_NT_STORE 1
+#endif
+#ifndef RMS_RESFWD_NT_LOAD
+#define RMS_RESFWD_NT_LOAD 1
+#endif
+#ifndef RMS_RESFWD_NT_STORE
+#define RMS_RESFWD_NT_STORE 1
+#endif
+// Row blocks in flight per workgroup beyond the one being finished (1 or 2).
+#ifndef RMS_FWD_PREFETCH
+#define RMS_FWD_PREFETCH 1
+#endif
 
 namespace rms {
 
@@ -35,6 +54,9 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
     constexpr int E = NCH * VEC;
     constexpr bool kCacheW = E * WG <= 32768;
     constexpr bool kPrefetch = E * WG <= 32768;
+    constexpr bool kNtLoad = RES ? RMS_RESFWD_NT_LOAD != 0 : RMS_FWD_NT_LOAD != 0;
+    constexpr bool kNtStore = RES ? RMS_RESFWD_NT_STORE != 0 : RMS_FWD_NT_STORE != 0;
+    constexpr int kDepth = kPrefetch ? RMS_FWD_PREFETCH : 0;
     __shared__ double red[TEAM > kWave ? R * NWT : 1];
 
     const int tid = threadIdx.x;
@@ -63,19 +85,30 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
         for (int c = 0; c < NCH; ++c) {
             const int col = (c * TEAM + lt) * VEC;
             const bool ok = active && col < H;
-            q.x[c] = ok ? load_pack<T, VEC>(x + off + col) : zero_pack<T, VEC>();
-            if constexpr (RES) q.r[c] = ok ? load_pack<T, VEC>(res + off + col) : zero_pack<T, VEC>();
+            q.x[c] = ok ? load_pack<T, VEC, kNtLoad>(x + off + col) : zero_pack<T, VEC>();
+            if constexpr (RES)
+                q.r[c] = ok ? load_pack<T, VEC, kNtLoad>(res + off + col) : zero_pack<T, VEC>();
         }
     };
 
+    // Ring of row blocks in flight: cur is being finished, ahead[d] is block
+    // rb + (d + 1) * gridDim.x (loads issued kDepth blocks ahead).
     RowRegs cur;
+    RowRegs ahead[kDepth > 0 ? kDepth : 1];
     int64_t rb = blockIdx.x;
-    if (kPrefetch && rb < nrb) load_row(rb, cur);
+    if constexpr (kDepth > 0) {
+        if (rb < nrb) load_row(rb, cur);
+#pragma unroll
+        for (int d = 0; d + 1 < kDepth; ++d) {
+            const int64_t b = rb + (d + 1) * (int64_t)gridDim.x;
+            if (b < nrb) load_row(b, ahead[d]);
+        }
+    }
     while (rb < nrb) {
         const int64_t nb = rb + gridDim.x;
-        RowRegs nxt;
-        if constexpr (kPrefetch) {
-            if (nb < nrb) load_row(nb, nxt);
+        if constexpr (kDepth > 0) {
+            const int64_t fb = rb + kDepth * (int64_t)gridDim.x;
+            if (fb < nrb) load_row(fb, ahead[kDepth - 1]);
         } else {
             load_row(rb, cur);
         }
@@ -94,7 +127,7 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) v[c][k] = round_to(v[c][k] + rv[k], (T*)nullptr);
                 const int col = (c * TEAM + lt) * VEC;
-                if (active && col < H) store_vec<T, VEC>(h + off + col, v[c]);
+                if (active && col < H) store_vec<T, VEC, kNtStore>(h + off + col, v[c]);
             }
 #pragma unroll
             for (int k = 0; k < VEC; ++k) ss += sq64(v[c][k], (T*)nullptr);
@@ -115,10 +148,14 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
             }
 #pragma unroll
             for (int k = 0; k < VEC; ++k) o[k] = (v[c][k] * rf) * wc[k];
-            if (active && col < H) store_vec<T, VEC>(y + off + col, o);
+            if (active && col < H) store_vec<T, VEC, kNtStore>(y + off + col, o);
         }
 
-        if constexpr (kPrefetch) cur = nxt;
+        if constexpr (kDepth > 0) {
+            cur = ahead[0];
+#pragma unroll
+            for (int d = 0; d + 1 < kDepth; ++d) ahead[d] = ahead[d + 1];
+        }
         rb = nb;
     }
 }
