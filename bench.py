@@ -278,24 +278,34 @@ def load_traffic(kernel_key):
 
 # ---------------------------------------------------------------- suite
 
-def time_calls(calls_per_set, k, reps, warmup, stream):
-    """Per-call event timing over rotating sets: list of µs per repetition,
-    one list entry per call in the group."""
+def time_calls(calls_per_set, k, reps, warmup, stream, burst=16):
+    """Per-launch µs of each call group over rotating sets: `reps` bursts of
+    `burst` back-to-back groups, events only at the burst ends.  Returns one
+    list (µs per group, one entry per burst) for each prefix of the group:
+    entry j times calls 0..j together, so a group (a, b) gives a alone and
+    a followed by b."""
     import torch
     for i in range(warmup):
         for c in calls_per_set[i % k]:
             run(c)
     torch.cuda.synchronize()
     n = len(calls_per_set[0])
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(reps)]
-    for i in range(reps):
-        grp = calls_per_set[i % k]
-        ev[i][0].record(stream)
-        for j, c in enumerate(grp):
-            run(c)
-            ev[i][j + 1].record(stream)
-    torch.cuda.synchronize()
-    return [[ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(reps)] for j in range(n)]
+    out = []
+    for j in range(n):
+        res = []
+        for r in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(burst):
+                grp = calls_per_set[(r * burst + i) % k]
+                for c in grp[: j + 1]:
+                    run(c)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) * 1e3 / burst)
+        out.append(res)
+    return out
 
 
 def summarise(name, us, nbytes, extra=None):
@@ -310,7 +320,7 @@ def summarise(name, us, nbytes, extra=None):
     return d
 
 
-def suite(path, reps=200, warmup=20):
+def suite(path, reps=30, warmup=20):
     import torch
     from bwd_rmsnorm_fwd_amd import synth
 
@@ -327,14 +337,19 @@ def suite(path, reps=200, warmup=20):
         sets = Sets(wl)
         C = Calls(sets, stream)
         e = sets.e
-        groups = [(C.fwd(s), C.bwd_rows(s), C.dw_reduce(s)) for s in sets.sets]
-        tf, tr, td = time_calls(groups, sets.k, reps, warmup, stream)
-        tb = [a + b for a, b in zip(tr, td)]
         meta = {"workload": name, "cold_sets": sets.k}
+        (tf,) = time_calls([(C.fwd(s),) for s in sets.sets], sets.k, reps, warmup, stream)
+        tr, tb = time_calls([(C.bwd_rows(s), C.dw_reduce(s)) for s in sets.sets], sets.k, reps,
+                            warmup, stream)
+        (td,) = time_calls([(C.dw_reduce(s),) for s in sets.sets], sets.k, reps, warmup, stream)
+        (ts, ) = time_calls([(C.fwd(s), C.bwd_rows(s), C.dw_reduce(s)) for s in sets.sets][:],
+                            sets.k, reps, warmup, stream)[2:]
         emit(summarise(f"{name}/fwd", tf, fwd_bytes(wl.rows, wl.H, e), meta))
         emit(summarise(f"{name}/bwd_rows", tr, bwd_rows_bytes(wl.rows, wl.H, e), meta))
         emit(summarise(f"{name}/dw_reduce", td, wl.H * e, meta))
         emit(summarise(f"{name}/bwd", tb, bwd_bytes(wl.rows, wl.H, e), meta))
+        emit(summarise(f"{name}/step_fwd_bwd", ts,
+                       fwd_bytes(wl.rows, wl.H, e) + bwd_bytes(wl.rows, wl.H, e), meta))
         # Warm-cache forward (same buffers every call): labelled, not HBM.
         (wf,) = time_calls([(C.fwd(sets.sets[0]),)], 1, reps, warmup, stream)
         emit(summarise(f"{name}/fwd_warm_cache", wf, fwd_bytes(wl.rows, wl.H, e),
@@ -345,11 +360,10 @@ def suite(path, reps=200, warmup=20):
     wl = synth.WORKLOADS["c4_bf16_residual_16384x4096"]
     sets = Sets(wl, residual=True, dres=True)
     C = Calls(sets, stream)
-    groups = [(C.residual_fwd(s), C.bwd_rows(s, x_key="h", dres=True), C.dw_reduce(s))
-              for s in sets.sets]
-    tf, tr, td = time_calls(groups, sets.k, reps, warmup, stream)
-    tb = [a + b for a, b in zip(tr, td)]
     meta = {"workload": wl.name, "cold_sets": sets.k}
+    (tf,) = time_calls([(C.residual_fwd(s),) for s in sets.sets], sets.k, reps, warmup, stream)
+    tr, tb = time_calls([(C.bwd_rows(s, x_key="h", dres=True), C.dw_reduce(s)) for s in sets.sets],
+                        sets.k, reps, warmup, stream)
     emit(summarise(f"{wl.name}/residual_fwd", tf, fwd_bytes(wl.rows, wl.H, 2, residual=True), meta))
     emit(summarise(f"{wl.name}/bwd_rows_dres", tr, bwd_rows_bytes(wl.rows, wl.H, 2, dres=True), meta))
     emit(summarise(f"{wl.name}/bwd_dres", tb, bwd_bytes(wl.rows, wl.H, 2, dres=True), meta))
@@ -398,6 +412,9 @@ def main():
     ap.add_argument("--suite", default=None, help="also measure every workload into this file")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-ref-mb", type=int, default=0,
+                    help="after the step, run a plain device copy of this many MiB (reference "
+                         "kernel of known size for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -456,6 +473,14 @@ def main():
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     if args.suite:
         suite(args.suite)
+    if args.copy_ref_mb:
+        n = args.copy_ref_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_ref_bytes"] = n
     print(json.dumps(line), flush=True)
 
 

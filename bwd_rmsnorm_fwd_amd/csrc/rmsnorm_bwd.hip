@@ -27,14 +27,14 @@
 #include "common.hpp"
 #include "launch.hpp"
 
-// Streaming (nontemporal) access to the row tensors: dy/x/dres loads, dx
-// stores.  Measured best: loads only for the plain backward, loads and
-// stores with a residual-stream gradient.
+// Streaming (nontemporal) access to the row tensors: dy/x/dres loads and
+// dx stores (measured best for a forward + backward step: dx lines left
+// dirty in the caches are otherwise written back during the next kernel).
 #ifndef RMS_BWD_NT_LOAD
 #define RMS_BWD_NT_LOAD 1
 #endif
 #ifndef RMS_BWD_NT_STORE
-#define RMS_BWD_NT_STORE 0
+#define RMS_BWD_NT_STORE 1
 #endif
 #ifndef RMS_DRES_NT_LOAD
 #define RMS_DRES_NT_LOAD 1
