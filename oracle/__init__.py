@@ -12,7 +12,8 @@ Sources:
   P1 = "训推加速 Qwen3 实战：从“调包”到手写 Triton Kernel（含 backward）"
        (iqiancheng.github.io): §4.1 forward definition, §5.3 backward.
   P2 = trdm.cn/news/483216, hand-written Triton decode kernels: §2.1 the
-       residual_add -> rms_norm pair and the planned fused kernel.
+       residual_add -> rms_norm pair and the planned fused kernel; §3.1 the
+       decode projection y = A x (computed there with split-K).
 
 Pinned by tests/test_oracle_pins.py (closed forms, invariants, central finite
 differences, a hand-derived worked example and library rounding routines).
@@ -68,6 +69,8 @@ def _load():
     lib.oracle_rmsnorm_residual_fwd.restype = None
     lib.oracle_rmsnorm_bwd.argtypes = [dp, dp, dp, dp, dp, i64, i64, ctypes.c_double, dp, dp]
     lib.oracle_rmsnorm_bwd.restype = None
+    lib.oracle_gemv.argtypes = [dp, dp, i64, i64, dp]
+    lib.oracle_gemv.restype = None
     _lib = lib
     return lib
 
@@ -136,3 +139,14 @@ def rmsnorm_bwd(dy, x, w, eps, rstd=None, dres=None):
     _load().oracle_rmsnorm_bwd(
         _ptr(dy), _ptr(x), _ptr(w), _ptr(rstd), _ptr(dres), rows, H, float(eps), _ptr(dx), _ptr(dw))
     return dx, dw
+
+
+def gemv(A, x):
+    """y[n] = sum_k A[n][k] x[k] (plain dot products, natural order)."""
+    A = np.ascontiguousarray(A, dtype=np.float64)
+    N, K = A.shape
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    assert x.shape == (K,)
+    y = np.empty(N, dtype=np.float64)
+    _load().oracle_gemv(_ptr(A), _ptr(x), N, K, _ptr(y))
+    return y

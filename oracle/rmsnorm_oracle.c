@@ -14,7 +14,8 @@
  *        §5.3 (backward derivation), §5.4 (dw as a cross-row sum).
  *   P2 = the trdm.cn write-up of hand-written Triton decode kernels
  *        (www.trdm.cn/news/483216), §2.1 (residual_add followed by rms_norm,
- *        and the planned fused residual + RMSNorm kernel).
+ *        and the planned fused residual + RMSNorm kernel), §3.1 (the decode
+ *        projection as a matrix-vector product, computed with split-K).
  *
  * Every loop runs in natural index order; no blocking, no reordering, no
  * parallelism.  Inputs are the exact values of the (already quantised) I/O
@@ -114,5 +115,16 @@ void oracle_rmsnorm_bwd(const double *dy, const double *x, const double *w,
             dx[i * H + j] = g;
             dw[j] += dyr[j] * xr[j] * r;
         }
+    }
+}
+
+/* Decode projection (P2 §3.1): y[n] = sum_k A[n][k] * x[k], A row-major
+ * [N][K], x [K], y [N].  Splitting K into segments (the split-K scheme) only
+ * regroups this sum; the definition is the plain dot product per row. */
+void oracle_gemv(const double *A, const double *x, int64_t N, int64_t K, double *y) {
+    for (int64_t n = 0; n < N; ++n) {
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k) s += A[n * K + k] * x[k];
+        y[n] = s;
     }
 }

@@ -383,3 +383,37 @@ def test_residual_bf16_equals_library_add_then_cast():
     assert np.array_equal(h, ref)
     y2, rs2 = oracle.rmsnorm_fwd(h, w, 1e-6)
     assert np.array_equal(y, y2) and np.array_equal(rs, rs2)
+
+
+# ---------------------------------------------------------------- decode projection
+
+def test_gemv_identity_and_constant():
+    """A = I gives y = x; a constant matrix gives y_n = c * sum(x)."""
+    rng = _rng(20)
+    x = rng.standard_normal(37)
+    assert np.array_equal(oracle.gemv(np.eye(37), x), x)
+    y = oracle.gemv(np.full((5, 37), 0.25), x)
+    np.testing.assert_allclose(y, 0.25 * np.sum(x), rtol=1e-13)
+
+
+def test_gemv_matches_library_matmul():
+    rng = _rng(21)
+    A = rng.standard_normal((64, 896))
+    x = rng.standard_normal(896)
+    np.testing.assert_allclose(oracle.gemv(A, x), A @ x, rtol=1e-12, atol=1e-12)
+
+
+def test_gemv_worked_example_and_linearity():
+    # [[1, 2, 3], [4, 5, 6]] @ [1, -1, 2] = [1 - 2 + 6, 4 - 5 + 12] = [5, 11]
+    A = np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]])
+    assert oracle.gemv(A, np.array([1.0, -1.0, 2.0])).tolist() == [5.0, 11.0]
+    rng = _rng(22)
+    A = rng.standard_normal((9, 13))
+    u, v = rng.standard_normal(13), rng.standard_normal(13)
+    np.testing.assert_allclose(oracle.gemv(A, 2 * u - 3 * v),
+                               2 * oracle.gemv(A, u) - 3 * oracle.gemv(A, v), rtol=1e-12, atol=1e-12)
+    # Row n of the output depends on row n of A only (no transposed index).
+    A2 = A.copy()
+    A2[4] *= -1
+    y, y2 = oracle.gemv(A, u), oracle.gemv(A2, u)
+    assert y2[4] == -y[4] and np.array_equal(np.delete(y, 4), np.delete(y2, 4))
