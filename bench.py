@@ -141,10 +141,11 @@ class Calls:
                 (p(s["x"]), p(s["res"]), p(s["w"]), p(s["h"]), p(s["y"]), p(s["rstd"]), self.rows,
                  self.H, self.eps, self.code, self.stream))
 
-    def bwd_rows(self, s, x_key="x", dres=False):
+    def bwd_rows(self, s, x_key="x", dres=False, saved_rstd=True):
         p = self.p
         return (self.L.rmsnorm_bwd_rows,
-                (p(s["dy"]), p(s[x_key]), p(s["w"]), p(s["rstd"]), p(s.get("dres")) if dres else None,
+                (p(s["dy"]), p(s[x_key]), p(s["w"]), p(s["rstd"]) if saved_rstd else None,
+                 p(s.get("dres")) if dres else None,
                  p(s["dx"]), p(s["ws"]), self.sets.ws_bytes, self.rows, self.H, self.eps, self.code,
                  self.stream))
 
@@ -171,12 +172,30 @@ def run(call):
 
 # ---------------------------------------------------------------- main benchmark
 
+def step_plan(C, sets, residual=False):
+    """Launch plan of one step per rotation slot: the forward of set i and the
+    backward of set i + k/2 (whose forward ran k/2 steps earlier), so that no
+    kernel reads data another kernel touched in the last ~0.5 GiB of traffic;
+    the backward uses the statistic its set's forward saved."""
+    k = sets.k
+    plan = []
+    for i in range(k):
+        f = sets.sets[i]
+        b = sets.sets[(i + k // 2) % k]
+        if residual:
+            plan.append((C.residual_fwd(f), C.bwd_rows(b, x_key="h", dres=True), C.dw_reduce(b)))
+        else:
+            plan.append((C.fwd(f), C.bwd_rows(b), C.dw_reduce(b)))
+    return plan
+
+
 def bench_step(steps, warmup):
     """The headline step on the bf16 4096 x 4096 workload.
 
     Region 1 times `steps` steps (forward, backward row pass, dw reduce) back
     to back, bracketed by synchronisation, with nothing else enqueued between
-    the launches.  Region 2 times each kernel on its own: `steps` launches back
+    the launches; each step's backward works on a different buffer set than its
+    forward (see step_plan), so both read their inputs from HBM.  Region 2 times each kernel on its own: `steps` launches back
     to back over the same rotating buffers, bracketed by HIP events recorded
     on the stream the kernels run on; the average per launch is the kernel's
     duration plus the small dispatch gap between launches."""
@@ -187,9 +206,9 @@ def bench_step(steps, warmup):
     sets = Sets(wl)
     stream = torch.cuda.current_stream()
     C = Calls(sets, stream)
-    plan = [(C.fwd(s), C.bwd_rows(s), C.dw_reduce(s)) for s in sets.sets]
+    plan = step_plan(C, sets)
 
-    for i in range(warmup):
+    for i in range(max(warmup, sets.k)):
         f, b, r = plan[i % sets.k]
         run(f); run(b); run(r)
     torch.cuda.synchronize()
@@ -342,19 +361,24 @@ def suite(path, reps=30, warmup=20):
         tr, tb = time_calls([(C.bwd_rows(s), C.dw_reduce(s)) for s in sets.sets], sets.k, reps,
                             warmup, stream)
         (td,) = time_calls([(C.dw_reduce(s),) for s in sets.sets], sets.k, reps, warmup, stream)
-        (ts, ) = time_calls([(C.fwd(s), C.bwd_rows(s), C.dw_reduce(s)) for s in sets.sets][:],
-                            sets.k, reps, warmup, stream)[2:]
+        (ts, ) = time_calls(step_plan(C, sets), sets.k, reps, max(warmup, sets.k), stream)[2:]
         emit(summarise(f"{name}/fwd", tf, fwd_bytes(wl.rows, wl.H, e), meta))
         emit(summarise(f"{name}/bwd_rows", tr, bwd_rows_bytes(wl.rows, wl.H, e), meta))
         emit(summarise(f"{name}/dw_reduce", td, wl.H * e, meta))
         emit(summarise(f"{name}/bwd", tb, bwd_bytes(wl.rows, wl.H, e), meta))
         emit(summarise(f"{name}/step_fwd_bwd", ts,
                        fwd_bytes(wl.rows, wl.H, e) + bwd_bytes(wl.rows, wl.H, e), meta))
+        # Backward that recomputes r from x instead of reading the saved rstd
+        # (4 bytes per row fewer; one more row reduction).
+        (tq,) = time_calls([(C.bwd_rows(s, saved_rstd=False),) for s in sets.sets], sets.k, reps,
+                           warmup, stream)
+        emit(summarise(f"{name}/bwd_rows_recompute_rstd", tq,
+                       bwd_rows_bytes(wl.rows, wl.H, e) - 4 * wl.rows, meta))
         # Warm-cache forward (same buffers every call): labelled, not HBM.
         (wf,) = time_calls([(C.fwd(sets.sets[0]),)], 1, reps, warmup, stream)
         emit(summarise(f"{name}/fwd_warm_cache", wf, fwd_bytes(wl.rows, wl.H, e),
                        {"workload": name, "note": "same buffers each call; not HBM-bound"}))
-        del sets, C, groups
+        del sets, C
         torch.cuda.empty_cache()
 
     wl = synth.WORKLOADS["c4_bf16_residual_16384x4096"]
@@ -367,7 +391,7 @@ def suite(path, reps=30, warmup=20):
     emit(summarise(f"{wl.name}/residual_fwd", tf, fwd_bytes(wl.rows, wl.H, 2, residual=True), meta))
     emit(summarise(f"{wl.name}/bwd_rows_dres", tr, bwd_rows_bytes(wl.rows, wl.H, 2, dres=True), meta))
     emit(summarise(f"{wl.name}/bwd_dres", tb, bwd_bytes(wl.rows, wl.H, 2, dres=True), meta))
-    del sets, C, groups
+    del sets, C
     torch.cuda.empty_cache()
 
     # Decode: 10k back-to-back calls on one stream, µs per call.
@@ -397,6 +421,95 @@ def suite(path, reps=30, warmup=20):
         emit({"name": f"{wl.name}/{label}", "us_per_call": round(us, 3), "calls": ncalls,
               "launches_per_call": 1 if splits == 0 else 2,
               "bytes": fwd_bytes(1, wl.H, 2), "workload": wl.name})
+        # The same calls captured once in a HIP graph (100 per graph) and
+        # replayed: the host launch cost per call disappears.
+        per_graph, replays = 100, ncalls // 100
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        Cg = Calls(sets, cs)
+        gcall = Cg.fwd(s) if splits == 0 else Cg.splitrow(s, partials, splits)
+        with torch.cuda.stream(cs):
+            for _ in range(10):
+                run(gcall)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cs):
+            for _ in range(per_graph):
+                run(gcall)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ug = e0.elapsed_time(e1) * 1e3 / (per_graph * replays)
+        emit({"name": f"{wl.name}/{label}_hip_graph", "us_per_call": round(ug, 3),
+              "calls": per_graph * replays, "calls_per_graph": per_graph,
+              "launches_per_call": 1 if splits == 0 else 2,
+              "bytes": fwd_bytes(1, wl.H, 2), "workload": wl.name})
+        del g
+    del sets, C
+    torch.cuda.empty_cache()
+
+    # Split-K decode projection (q_proj 896 -> 1024): 10k calls per split
+    # count, plain and captured in a HIP graph.
+    import numpy as np
+    from bwd_rmsnorm_fwd_amd import binding as B
+    gw = synth.GEMV_WORKLOADS["q_proj_bf16_1024x896"]
+    A = torch.from_numpy(gw.A().view(np.int16)).view(torch.bfloat16).cuda()
+    xv = torch.from_numpy(gw.x().view(np.int16)).view(torch.bfloat16).cuda()
+    yv = torch.empty(gw.N, dtype=torch.bfloat16, device="cuda")
+    L = B.lib()
+    gbytes = (gw.N * gw.K + gw.K + gw.N) * 2
+    for splits in gw.splits:
+        parts = torch.empty(max(B.decode_gemv_partials_count(gw.N, splits), 1), device="cuda")
+
+        def gcall(st):
+            return (L.decode_gemv_splitk,
+                    (ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(xv.data_ptr()),
+                     ctypes.c_void_p(yv.data_ptr()), ctypes.c_void_p(parts.data_ptr()),
+                     parts.numel(), gw.N, gw.K, splits, B.BF16, ctypes.c_void_p(st.cuda_stream)))
+        call = gcall(stream)
+        for _ in range(200):
+            run(call)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(ncalls):
+            run(call)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / ncalls
+        emit({"name": f"{gw.name}/gemv_S{splits}", "us_per_call": round(us, 3), "calls": ncalls,
+              "launches_per_call": 1 if splits == 1 else 2, "bytes": gbytes,
+              "GB_s": round(gbytes / us / 1e3, 1), "workload": gw.name})
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        c2 = gcall(cs)
+        with torch.cuda.stream(cs):
+            for _ in range(10):
+                run(c2)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cs):
+            for _ in range(100):
+                run(c2)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(ncalls // 100):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ug = e0.elapsed_time(e1) * 1e3 / ncalls
+        emit({"name": f"{gw.name}/gemv_S{splits}_hip_graph", "us_per_call": round(ug, 3),
+              "calls": ncalls, "launches_per_call": 1 if splits == 1 else 2, "bytes": gbytes,
+              "GB_s": round(gbytes / ug / 1e3, 1), "workload": gw.name})
+        del g
     with open(path, "w") as f:
         for d in out:
             f.write(json.dumps(d) + "\n")

@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
         "rmsnorm_splitrow_partials_count": ([i64, i32], sz),
         "rmsnorm_fwd_splitrow": ([vp, vp, vp, vp, vp, sz, i64, i64, f32, i32, i32, vp], i32),
         "rmsnorm_status_str": ([i32], ctypes.c_char_p),
+        "decode_gemv_partials_count": ([i64, i32], sz),
+        "decode_gemv_splitk": ([vp, vp, vp, vp, sz, i64, i64, i32, i32, vp], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -212,3 +214,27 @@ def rmsnorm_fwd_splitrow(x, w, y, rstd, partials, splits: int, eps: float = 1e-6
     _check("rmsnorm_fwd_splitrow",
            lib().rmsnorm_fwd_splitrow(_p(x), _p(w), _p(y), _p(rstd), _p(partials), count, rows, H,
                                       float(eps), int(splits), _dtype_code(x), _stream(stream)))
+
+
+# ---------------------------------------------------------------- decode projection
+
+def decode_gemv_partials_count(N: int, splits: int) -> int:
+    return int(lib().decode_gemv_partials_count(int(N), int(splits)))
+
+
+def decode_gemv_splitk(A, x, y, partials=None, splits: int = 1, stream=None) -> None:
+    """y = A x (A [N][K]) with K split in `splits` segments (fp32 partials,
+    then the fixed-order splitk_reduce pass)."""
+    import torch
+    _contig(A, x, y, partials)
+    if A.dim() != 2:
+        raise ValueError("A must be [N][K]")
+    N, K = A.shape
+    _expect("x", x, K, A.dtype)
+    _expect("y", y, N, A.dtype)
+    if partials is not None and partials.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    count = 0 if partials is None else partials.numel()
+    _check("decode_gemv_splitk",
+           lib().decode_gemv_splitk(_p(A), _p(x), _p(y), _p(partials), count, N, K, int(splits),
+                                    _dtype_code(A), _stream(stream)))

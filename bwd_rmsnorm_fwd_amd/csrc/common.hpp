@@ -126,6 +126,10 @@ __device__ __forceinline__ void store_vec(T* p, const float (&f)[VEC]) {
 // fp32 multiply loses nothing; for fp32 inputs they are formed in fp64.
 __device__ __forceinline__ double sq64(float v, float*) { return (double)v * (double)v; }
 __device__ __forceinline__ double sq64(float v, bf16_t*) { return (double)(v * v); }
+__device__ __forceinline__ double prod2_64(float a, float b, float*) {
+    return (double)a * (double)b;
+}
+__device__ __forceinline__ double prod2_64(float a, float b, bf16_t*) { return (double)(a * b); }
 __device__ __forceinline__ double prod3_64(float a, float b, float c, float*) {
     return (double)a * (double)b * (double)c;
 }

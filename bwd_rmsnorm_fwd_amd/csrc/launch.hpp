@@ -67,4 +67,18 @@ hipError_t launch_dw_reduce(DType dt, const float* partial, int G, int ldp, int 
 hipError_t launch_splitrow(DType dt, int vec, const FwdArgs& a, float* partials, int splits,
                            hipStream_t s);
 
+struct GemvArgs {
+    const void* A;    // [N][K]
+    const void* x;    // [K]
+    void* y;          // [N]
+    float* partials;  // [splits][N] (unused when splits == 1)
+    int N;
+    int K;
+    int seg;          // segment length (multiple of the vector width)
+    int splits;
+    int team;         // lanes per row (power of two, <= 64)
+};
+
+hipError_t launch_gemv(DType dt, int vec, const GemvArgs& a, hipStream_t s);
+
 }  // namespace rms

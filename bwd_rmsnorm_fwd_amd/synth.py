@@ -137,3 +137,28 @@ def small_case(rows: int, H: int, dtype: str = BF16, seed: int = 7, eps: float =
     s = 1000 * seed
     return Workload(f"case_{dtype}_{rows}x{H}_s{seed}", dtype, rows, H, eps,
                     s + 1, s + 2, s + 3, s + 4, s + 5, outlier_frac, s + 6, dy_sigma, residual)
+
+
+@dataclass(frozen=True)
+class GemvWorkload:
+    """Decode projection y = A x: A [N][K] ~ N(0, sigma_a^2), x [K] ~ N(0, 1)."""
+    name: str
+    dtype: str
+    N: int
+    K: int
+    seed_a: int
+    seed_x: int
+    sigma_a: float = 0.02
+    splits: tuple = (1, 4, 8, 16)
+
+    def A(self):
+        return normal(self.seed_a, (self.N, self.K), self.sigma_a, self.dtype)
+
+    def x(self):
+        return normal(self.seed_x, (self.K,), 1.0, self.dtype)
+
+
+# P2's q_proj at batch 1: hidden 896 -> 1024 outputs, split 1/4/8/16.
+GEMV_WORKLOADS = {
+    "q_proj_bf16_1024x896": GemvWorkload("q_proj_bf16_1024x896", BF16, 1024, 896, 601, 602),
+}

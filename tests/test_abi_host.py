@@ -20,7 +20,8 @@ def declared_functions():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(rmsnorm_\w+)\s*\(", text, flags=re.M)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b((?:rmsnorm|decode_gemv)_\w+)\s*\(",
+                            text, flags=re.M)
     return sorted(set(names))
 
 
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     for fn in declared_functions():
         assert hasattr(L, fn), f"{fn} declared in include/ but not exported"
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r"\bT (rmsnorm_\w+)", out))
+    exported = set(re.findall(r"\bT ((?:rmsnorm|decode_gemv)_\w+)", out))
     assert set(declared_functions()) == exported, exported ^ set(declared_functions())
 
 
@@ -116,6 +117,22 @@ def test_splitrow_validation():
     assert f(A, A, A, None, A, 3, 1, 896, 1e-6, 4, B.BF16, None) == B.EWORKSPACE    # too few
     assert f(A, A, A, None, None, 4, 1, 896, 1e-6, 4, B.BF16, None) == B.EWORKSPACE
     assert f(A, A, A, None, A, 4, 0, 896, 1e-6, 4, B.BF16, None) == B.EINVAL        # rows = 0
+
+
+def test_gemv_validation():
+    L = B.lib()
+    A = ctypes.c_void_p(0x10000)
+    assert L.decode_gemv_partials_count(1024, 4) == 4096
+    assert L.decode_gemv_partials_count(1024, 1) == 0
+    assert L.decode_gemv_partials_count(0, 4) == 0
+    f = L.decode_gemv_splitk
+    assert f(A, A, A, A, 4096, 1024, 896, 0, B.BF16, None) == B.EINVAL        # splits = 0
+    assert f(A, A, A, A, 4096, 1024, 896, 65, B.BF16, None) == B.EINVAL       # > max
+    assert f(A, A, A, A, 4095, 1024, 896, 4, B.BF16, None) == B.EWORKSPACE    # too few partials
+    assert f(A, A, A, None, 0, 1024, 896, 4, B.BF16, None) == B.EWORKSPACE
+    assert f(A, None, A, None, 0, 1024, 896, 1, B.BF16, None) == B.EINVAL     # x missing
+    assert f(A, A, A, None, 0, 0, 896, 1, B.BF16, None) == B.EINVAL           # N = 0
+    assert f(MIS, A, A, None, 0, 8, 896, 1, B.BF16, None) == B.EALIGN
 
 
 def test_binding_rejects_mismatched_tensors():
