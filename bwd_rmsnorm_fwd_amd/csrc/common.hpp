@@ -75,6 +75,15 @@ __device__ __forceinline__ Pack<T, VEC> load_pack(const T* p) {
     return r;
 }
 
+// Make a packed register opaque to the optimiser: values unpacked from it
+// before this point are not reused after it, so the compiler re-derives them
+// (a shift or a mask per element) instead of keeping the float copies live
+// across a reduction.  Emits no instruction.
+template <typename T, int VEC>
+__device__ __forceinline__ void opaque(Pack<T, VEC>& p) {
+    if constexpr (VEC > 1) asm volatile("" : "+v"(p.v));
+}
+
 template <typename T, int VEC>
 __device__ __forceinline__ Pack<T, VEC> zero_pack() {
     Pack<T, VEC> r;

@@ -67,6 +67,11 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     constexpr bool kNtLoad = DRES ? RMS_DRES_NT_LOAD != 0 : RMS_BWD_NT_LOAD != 0;
     constexpr bool kNtStore = DRES ? RMS_DRES_NT_STORE != 0 : RMS_BWD_NT_STORE != 0;
     constexpr int kDepth = kPrefetch ? RMS_BWD_PREFETCH : 0;
+    // 512-lane tiles re-derive the unpacked row in pass B instead of keeping
+    // it live across the row reduction; that fits two workgroups per CU (the
+    // plain backward stays within 128 VGPRs), which bwd_groups() then uses.
+    // Elsewhere keeping the floats live measured faster.
+    constexpr bool kLean = TEAM == 512;
     // Teams combine their dw sums either side by side ([R][HT], summed per
     // column in team order) when that fits in 32 KiB, or one after another
     // into a single [HT] row.
@@ -158,6 +163,13 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
             for (int k = 0; k < VEC; ++k) {
                 cs += prod3_64(wc[k], dyv[k], xv[k], (T*)nullptr);
                 if (!has_rstd) ss += sq64(xv[k], (T*)nullptr);
+            }
+        }
+        if constexpr (kLean) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                opaque(cur.x[c]);
+                opaque(cur.dy[c]);
             }
         }
         cs = team_sum<TEAM>(cs, red);
@@ -322,10 +334,16 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict_
 #endif
 
 int bwd_groups(int64_t rows, int64_t H, DType dt) {
-    (void)H; (void)dt;
     if (rows <= 0) return 0;
-    int64_t g = (rows + RMS_BWD_MIN_ROWS_PER_GROUP - 1) / RMS_BWD_MIN_ROWS_PER_GROUP;
-    return (int)(g < RMS_BWD_MAX_GROUPS ? g : RMS_BWD_MAX_GROUPS);
+    // The tile of the 128-bit path decides the cap (also when a call falls
+    // back to scalar accesses, so the group count depends on the shape only):
+    // 512-lane tiles run two workgroups per CU, the others one.
+    Geometry g;
+    const int vec = dt == DType::F32 ? 4 : 8;
+    const int64_t cap = (choose_geometry(H, vec, &g) && g.team == 512) ? 2 * RMS_BWD_MAX_GROUPS
+                                                                          : RMS_BWD_MAX_GROUPS;
+    const int64_t n = (rows + RMS_BWD_MIN_ROWS_PER_GROUP - 1) / RMS_BWD_MIN_ROWS_PER_GROUP;
+    return (int)(n < cap ? n : cap);
 }
 
 int partial_ld(int64_t H) { return (int)((H + 63) / 64 * 64); }
