@@ -310,3 +310,49 @@ def test_graph_capture_replays_match_eager():
             assert torch.equal(out[k].view(torch.int16), ref[k].view(torch.int16)), (rep, k)
         assert torch.equal(dw.view(torch.int16), ref_dw.view(torch.int16))
         assert torch.equal(rstd, ref_r)
+
+
+@pytest.mark.parametrize("dtype,rows,H", [(synth.BF16, 3, 32768), (synth.BF16, 2, 65536),
+                                          (synth.BF16, 2, 30000), (synth.F32, 2, 16384),
+                                          (synth.F32, 1, 65536)])
+def test_widest_rows(dtype, rows, H):
+    """The 1024-lane tiles with 4-16 chunks per lane (their backward spills
+    registers: slower, still exact to the same bars) and H = RMSNORM_MAX_H."""
+    wl, x, w, dy, res, dres = _inputs(rows, H, dtype, seed=H + rows)
+    xd, wd, dyd, rd, drd = (to_dev(a, dtype) for a in (x, w, dy, res, dres))
+    h, y, dx = _empty(rows, H, dtype), _empty(rows, H, dtype), _empty(rows, H, dtype)
+    rstd = torch.empty(rows, device=DEV)
+    dw = torch.empty(H, dtype=torch_dtype(dtype), device=DEV)
+    B.rmsnorm_residual_fwd(xd, rd, wd, h, y, rstd, wl.eps)
+    B.rmsnorm_bwd(dyd, h, wd, rstd, drd, dx, dw, _ws(rows, H, dtype), wl.eps)
+    torch.cuda.synchronize()
+    kind = oracle.H_BF16 if dtype == synth.BF16 else oracle.H_F32
+    ho, yo, ro = oracle.rmsnorm_residual_fwd(synth.to_f64(x, dtype), synth.to_f64(res, dtype),
+                                             synth.to_f64(w, dtype), wl.eps, kind)
+    assert np.array_equal(f64(h), ho)
+    assert_output("y", f64(y), yo, dtype)
+    assert_rstd(f64(rstd), ro)
+    dxo, dwo = oracle.rmsnorm_bwd(synth.to_f64(dy, dtype), ho, synth.to_f64(w, dtype), wl.eps,
+                                  rstd=f64(rstd), dres=synth.to_f64(dres, dtype))
+    assert_output("dx", f64(dx), dxo, dtype)
+    assert_dw(f64(dw), dwo, dtype)
+
+
+def test_scalar_path_width_limit():
+    """Rows that miss the 128-bit path are limited to RMSNORM_MAX_H_SCALAR;
+    wider ones are refused, not mis-computed."""
+    H = B.MAX_H_SCALAR + 1                     # odd: scalar accesses
+    x = torch.zeros((2, H), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(H, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty_like(x)
+    with pytest.raises(B.RMSNormError) as e:
+        B.rmsnorm_fwd(x, w, y, None, 1e-6)
+    assert e.value.status == B.EUNSUPPORTED
+    H = B.MAX_H_SCALAR - 1                     # largest odd width that is served
+    wl, xa, wa, *_ = _inputs(2, H, synth.BF16, seed=5)
+    xd, wd = to_dev(xa, synth.BF16), to_dev(wa, synth.BF16)
+    y = _empty(2, H, synth.BF16)
+    B.rmsnorm_fwd(xd, wd, y, None, wl.eps)
+    torch.cuda.synchronize()
+    yo, _ = oracle.rmsnorm_fwd(synth.to_f64(xa, synth.BF16), synth.to_f64(wa, synth.BF16), wl.eps)
+    assert_output("y", f64(y), yo, synth.BF16)
