@@ -520,8 +520,11 @@ def suite(path, reps=30, warmup=20):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # The GPU needs a few hundred steps of load before its step time settles
+    # (measured: ~38-40 µs/step over the first 50 steps, 35 µs from ~300 on,
+    # flat to 5000), so the default warm-up is long.
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--suite", default=None, help="also measure every workload into this file")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -10,9 +10,9 @@
 //   run-to-run reproducibility.
 //
 // Design (MI355X):
-//   * Row pass: G persistent workgroups; workgroup g owns a contiguous range
-//     of rows, processed R rows at a time (one team per row, as in the
-//     forward), prefetching the next R rows while finishing the current.
+//   * Row pass: G persistent workgroups; rows go in blocks of R (one team
+//     per row, as in the forward) dealt round-robin to the workgroups, each
+//     prefetching its next block while finishing the current one.
 //     dy, x (and dres) are read once; rstd is the forward's saved statistic
 //     (or is recomputed from x when none is given).
 //   * The row sums c (and sum x^2 when recomputing) are exact fp32 products
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
                                                       const float* __restrict__ rstd,
                                                       const T* dres, T* dx,
                                                       float* __restrict__ partial, int64_t rows,
-                                                      int H, int ldp, int64_t rpg, float eps) {
+                                                      int H, int ldp, float eps) {
     constexpr int R = WG / TEAM;
     constexpr int NWT = TEAM > kWave ? TEAM / kWave : 1;
     constexpr int HT = TEAM * NCH * VEC;  // columns covered by one team
@@ -83,8 +83,13 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     const int team = tid / TEAM;
     const int lt = tid % TEAM;
     const bool has_rstd = rstd != nullptr;
-    const int64_t begin = (int64_t)blockIdx.x * rpg;
-    const int64_t end = begin + rpg < rows ? begin + rpg : rows;
+    // Row blocks of R rows are dealt round-robin: workgroup g takes blocks
+    // g, g + G, g + 2G, ..., so at any moment the workgroups stream
+    // neighbouring rows (measured 5-9% faster than contiguous row ranges per
+    // workgroup, which scatter the concurrent streams across memory).
+    const int64_t begin = (int64_t)blockIdx.x * R;
+    const int64_t stride = (int64_t)gridDim.x * R;
+    const int64_t end = rows;
 
     float wv[kCacheW ? NCH : 1][VEC];
     float acc[NCH][VEC];
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     };
 
     // Ring of row blocks in flight: cur is being finished, ahead[d] is the
-    // block (d + 1) * R rows further on (loaded kDepth blocks ahead).
+    // block d + 1 strides further on (loaded kDepth blocks ahead).
     RowRegs cur;
     RowRegs ahead[kDepth > 0 ? kDepth : 1];
     int64_t base = begin;
@@ -137,12 +142,12 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
         if (base < end) load_row(base, cur);
 #pragma unroll
         for (int d = 0; d + 1 < kDepth; ++d)
-            if (base + (d + 1) * R < end) load_row(base + (d + 1) * R, ahead[d]);
+            if (base + (d + 1) * stride < end) load_row(base + (d + 1) * stride, ahead[d]);
     }
     while (base < end) {
-        const int64_t nb = base + R;
+        const int64_t nb = base + stride;
         if constexpr (kDepth > 0) {
-            const int64_t fb = base + kDepth * R;
+            const int64_t fb = base + kDepth * stride;
             if (fb < end) load_row(fb, ahead[kDepth - 1]);
         } else {
             load_row(base, cur);
@@ -357,15 +362,14 @@ static hipError_t launch_rows_cfg(const BwdArgs& a, hipStream_t s) {
     constexpr int EB = NCH * VEC * (int)sizeof(T);
     constexpr int WGD = EB <= 16 ? 1024 : (EB <= 32 ? 512 : 256);
     constexpr int WG = TEAM > WGD ? TEAM : WGD;
-    const int64_t rpg = (a.rows + a.G - 1) / a.G;
     if (a.dres) {
         hipLaunchKernelGGL((bwd_rows_kernel<T, VEC, TEAM, NCH, WG, true>), dim3(a.G), dim3(WG), 0,
                            s, (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
-                           (const T*)a.dres, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, rpg, a.eps);
+                           (const T*)a.dres, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
     } else {
         hipLaunchKernelGGL((bwd_rows_kernel<T, VEC, TEAM, NCH, WG, false>), dim3(a.G), dim3(WG), 0,
                            s, (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
-                           (const T*)nullptr, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, rpg, a.eps);
+                           (const T*)nullptr, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
     }
     return hipGetLastError();
 }
