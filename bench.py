@@ -535,9 +535,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the RMSNorm path here is built and timed on a single "
-              "MI355X (rows shard across GPUs with no exchange except one dw all-reduce, which "
-              "this build does not implement); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the RMSNorm library runs on a single MI355X (rows "
+              "would shard across GPUs with no exchange except one dw all-reduce, which this "
+              "library does not provide); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -42,6 +42,10 @@
 #ifndef RMS_DRES_NT_STORE
 #define RMS_DRES_NT_STORE 1
 #endif
+// Smallest team of the register-trimmed, two-workgroups-per-CU tiles.
+#ifndef RMS_BWD_LEAN_MIN
+#define RMS_BWD_LEAN_MIN 512
+#endif
 // Row blocks in flight per workgroup beyond the one being finished (1 or 2).
 #ifndef RMS_BWD_PREFETCH
 #define RMS_BWD_PREFETCH 1
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     // it live across the row reduction; that fits two workgroups per CU (the
     // plain backward stays within 128 VGPRs), which bwd_groups() then uses.
     // Elsewhere keeping the floats live measured faster.
-    constexpr bool kLean = TEAM == 512;
+    constexpr bool kLean = TEAM >= RMS_BWD_LEAN_MIN && TEAM <= 512;
     // Teams combine their dw sums either side by side ([R][HT], summed per
     // column in team order) when that fits in 32 KiB, or one after another
     // into a single [HT] row.
@@ -345,8 +349,8 @@ int bwd_groups(int64_t rows, int64_t H, DType dt) {
     // 512-lane tiles run two workgroups per CU, the others one.
     Geometry g;
     const int vec = dt == DType::F32 ? 4 : 8;
-    const int64_t cap = (choose_geometry(H, vec, &g) && g.team == 512) ? 2 * RMS_BWD_MAX_GROUPS
-                                                                          : RMS_BWD_MAX_GROUPS;
+    const bool lean = choose_geometry(H, vec, &g) && g.team >= RMS_BWD_LEAN_MIN && g.team <= 512;
+    const int64_t cap = lean ? 2 * RMS_BWD_MAX_GROUPS : RMS_BWD_MAX_GROUPS;
     const int64_t n = (rows + RMS_BWD_MIN_ROWS_PER_GROUP - 1) / RMS_BWD_MIN_ROWS_PER_GROUP;
     return (int)(n < cap ? n : cap);
 }
