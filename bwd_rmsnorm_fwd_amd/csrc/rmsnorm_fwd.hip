@@ -63,6 +63,7 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
     const int team = tid / TEAM;
     const int lt = tid % TEAM;
     const int64_t nrb = (rows + R - 1) / R;
+    const double inv_h = 1.0 / (double)H;  // exact for power-of-two H
 
     float wv[kCacheW ? NCH : 1][VEC];
     if constexpr (kCacheW) {
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
             for (int k = 0; k < VEC; ++k) ss += sq64(v[c][k], (T*)nullptr);
         }
         ss = team_sum<TEAM>(ss, red);
-        const double r = 1.0 / sqrt(ss / (double)H + (double)eps);
+        const double r = rsqrt_f64(ss * inv_h + (double)eps);
         const float rf = (float)r;
         if (active && lt == 0 && rstd) rstd[row] = rf;
 #pragma unroll

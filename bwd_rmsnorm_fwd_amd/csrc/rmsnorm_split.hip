@@ -52,7 +52,7 @@ __global__ __launch_bounds__(WG) void split_finalize_kernel(const T* __restrict_
     const float* pr = partials + row * splits;
     double ss = 0.0;
     for (int s = 0; s < splits; ++s) ss += (double)pr[s];  // index order, never past `splits`
-    const double r = 1.0 / sqrt(ss / (double)H + (double)eps);
+    const double r = rsqrt_f64(ss * (1.0 / (double)H) + (double)eps);
     const float rf = (float)r;
     if (threadIdx.x == 0 && rstd) rstd[row] = rf;
     const T* xr = x + row * (int64_t)H;
