@@ -287,37 +287,48 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     }
 }
 
-// dw[j] = sum_{g < G} partial[g][j] in a fixed order.  A workgroup owns
-// kRedCols columns (kRedCL lanes x 4 columns, 128-bit loads) and kRedGL lanes
-// over g: lane gl adds rows g = gl, gl + kRedGL, ... in increasing g (eight
-// independent loads in flight per step), then the kRedGL lane sums of each
-// column are added in gl order.
-constexpr int kRedCL = 8;
-constexpr int kRedGL = 256 / kRedCL;
+// dw[j] = sum_{g < G} partial[g][j] in a fixed order.  A workgroup of
+// kRedWG lanes owns kRedCols columns (kRedCL lanes x 4 columns, 128-bit
+// loads) and kRedGL lanes over g: lane gl adds rows g = gl, gl + kRedGL, ...
+// in increasing g, kRedU independent loads in flight per step (rows past G
+// load as zero, which leaves the sum unchanged), then the kRedGL lane sums of
+// each column are added in gl order.
+#ifndef RMS_RED_CL
+#define RMS_RED_CL 8
+#endif
+#ifndef RMS_RED_WG
+#define RMS_RED_WG 256
+#endif
+#ifndef RMS_RED_UNROLL
+#define RMS_RED_UNROLL 8
+#endif
+constexpr int kRedCL = RMS_RED_CL;
+constexpr int kRedWG = RMS_RED_WG;
+constexpr int kRedU = RMS_RED_UNROLL;
+constexpr int kRedGL = kRedWG / kRedCL;
 constexpr int kRedCols = 4 * kRedCL;
+static_assert(kRedWG % kRedCL == 0 && 64 % kRedCols == 0, "reduce tile must divide ldp (multiple of 64)");
 
 template <typename T>
-__global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict__ partial, int G,
-                                                        int ldp, int H, T* __restrict__ dw) {
+__global__ __launch_bounds__(kRedWG) void dw_reduce_kernel(const float* __restrict__ partial, int G,
+                                                           int ldp, int H, T* __restrict__ dw) {
     __shared__ float part[kRedGL][kRedCols + 1];
     const int cl = threadIdx.x % kRedCL;
     const int gl = threadIdx.x / kRedCL;
-    // ldp is a multiple of 64, so col0 + 3 < ldp for every workgroup.
+    // ldp is a multiple of 64 and of kRedCols, so col0 + 3 < ldp for every workgroup.
     const int col0 = blockIdx.x * kRedCols + cl * 4;
     const float* base = partial + col0;
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    int g = gl;
-    for (; g + 7 * kRedGL < G; g += 8 * kRedGL) {
-        float4 p[8];
+    for (int g = gl; g < G; g += kRedU * kRedGL) {
+        float4 p[kRedU];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            p[u] = *reinterpret_cast<const float4*>(base + (int64_t)(g + u * kRedGL) * ldp);
+        for (int u = 0; u < kRedU; ++u) {
+            const int gu = g + u * kRedGL;
+            p[u] = gu < G ? *reinterpret_cast<const float4*>(base + (int64_t)gu * ldp)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) { a0 += p[u].x; a1 += p[u].y; a2 += p[u].z; a3 += p[u].w; }
-    }
-    for (; g < G; g += kRedGL) {
-        const float4 p = *reinterpret_cast<const float4*>(base + (int64_t)g * ldp);
-        a0 += p.x; a1 += p.y; a2 += p.z; a3 += p.w;
+        for (int u = 0; u < kRedU; ++u) { a0 += p[u].x; a1 += p[u].y; a2 += p[u].z; a3 += p[u].w; }
     }
     part[gl][cl * 4 + 0] = a0;
     part[gl][cl * 4 + 1] = a1;
@@ -327,7 +338,7 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict_
     if (threadIdx.x < kRedCols) {
         const int col = blockIdx.x * kRedCols + threadIdx.x;
         float sum = part[0][threadIdx.x];
-#pragma unroll
+#pragma unroll 16
         for (int j = 1; j < kRedGL; ++j) sum += part[j][threadIdx.x];
         if (col < H) {
             float o[1] = {sum};
@@ -403,10 +414,10 @@ hipError_t launch_dw_reduce(DType dt, const float* partial, int G, int ldp, int 
                             hipStream_t s) {
     const int grid = ldp / kRedCols;
     if (dt == DType::F32) {
-        hipLaunchKernelGGL((dw_reduce_kernel<float>), dim3(grid), dim3(256), 0, s, partial, G, ldp, H,
-                           (float*)dw);
+        hipLaunchKernelGGL((dw_reduce_kernel<float>), dim3(grid), dim3(kRedWG), 0, s, partial, G, ldp,
+                           H, (float*)dw);
     } else {
-        hipLaunchKernelGGL((dw_reduce_kernel<bf16_t>), dim3(grid), dim3(256), 0, s, partial, G, ldp,
+        hipLaunchKernelGGL((dw_reduce_kernel<bf16_t>), dim3(grid), dim3(kRedWG), 0, s, partial, G, ldp,
                            H, (bf16_t*)dw);
     }
     return hipGetLastError();
