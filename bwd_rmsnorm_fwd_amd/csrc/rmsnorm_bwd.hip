@@ -50,6 +50,10 @@
 #ifndef RMS_BWD_PREFETCH
 #define RMS_BWD_PREFETCH 1
 #endif
+// Nontemporal stores for the dw partial rows (read once, by the reduce pass).
+#ifndef RMS_BWD_PART_NT
+#define RMS_BWD_PART_NT 0
+#endif
 
 namespace rms {
 
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     // into a single [HT] row.
     constexpr bool kWideComb = R > 1 && R * HT <= 8192;
     __shared__ double red[TEAM > kWave ? 2 * R * NWT : 1];
-    __shared__ float comb[R == 1 ? 1 : (kWideComb ? R * HT : HT)];
+    __shared__ __align__(16) float comb[R == 1 ? 1 : (kWideComb ? R * HT : HT)];
 
     const int tid = threadIdx.x;
     const int team = tid / TEAM;
@@ -241,7 +245,16 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     }
 
     // One partial row per workgroup: combine the R teams in team order.
+    // With VEC > 1, H is a multiple of VEC, so groups of four columns that
+    // start below H end below H (and below HT); ldp is a multiple of 64.
     float* prow = partial + (int64_t)blockIdx.x * ldp;
+    constexpr bool kPartNt = RMS_BWD_PART_NT != 0;
+    auto store4 = [&](int col, float a, float b, float c, float d) {
+        u32x4 v;
+        v.x = __float_as_uint(a); v.y = __float_as_uint(b);
+        v.z = __float_as_uint(c); v.w = __float_as_uint(d);
+        st128<kPartNt>(prow + col, v);
+    };
     if constexpr (R == 1) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
@@ -252,8 +265,7 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
                 } else {
 #pragma unroll
                     for (int k = 0; k < VEC; k += 4)
-                        *reinterpret_cast<float4*>(prow + col + k) =
-                            make_float4(acc[c][k], acc[c][k + 1], acc[c][k + 2], acc[c][k + 3]);
+                        store4(col + k, acc[c][k], acc[c][k + 1], acc[c][k + 2], acc[c][k + 3]);
                 }
             }
         }
@@ -264,10 +276,21 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
             for (int k = 0; k < VEC; ++k) comb[team * HT + (c * TEAM + lt) * VEC + k] = acc[c][k];
         }
         __syncthreads();
-        for (int col = tid; col < H && col < HT; col += WG) {
-            float sum = comb[col];
-            for (int t = 1; t < R; ++t) sum += comb[t * HT + col];
-            prow[col] = sum;
+        if constexpr (VEC >= 4) {
+            for (int col = tid * 4; col < H; col += WG * 4) {
+                float4 sum = *reinterpret_cast<const float4*>(comb + col);
+                for (int t = 1; t < R; ++t) {
+                    const float4 v = *reinterpret_cast<const float4*>(comb + t * HT + col);
+                    sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+                }
+                store4(col, sum.x, sum.y, sum.z, sum.w);
+            }
+        } else {
+            for (int col = tid; col < H && col < HT; col += WG) {
+                float sum = comb[col];
+                for (int t = 1; t < R; ++t) sum += comb[t * HT + col];
+                prow[col] = sum;
+            }
         }
     } else {
         for (int t = 0; t < R; ++t) {
@@ -283,7 +306,14 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
             }
             __syncthreads();
         }
-        for (int col = tid; col < H && col < HT; col += WG) prow[col] = comb[col];
+        if constexpr (VEC >= 4) {
+            for (int col = tid * 4; col < H; col += WG * 4) {
+                const float4 v = *reinterpret_cast<const float4*>(comb + col);
+                store4(col, v.x, v.y, v.z, v.w);
+            }
+        } else {
+            for (int col = tid; col < H && col < HT; col += WG) prow[col] = comb[col];
+        }
     }
 }
 

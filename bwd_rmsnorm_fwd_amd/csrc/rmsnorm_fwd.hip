@@ -12,13 +12,25 @@
 // from HBM exactly once.  Loads/stores are 128-bit per lane and contiguous
 // across the team.  The sum of squares is exact-product fp32 accumulated in
 // fp64 per lane, reduced with DPP inside 16-lane rows and lane reads across
-// rows (LDS across wavefronts).  Workgroups are persistent up to a grid cap
-// and prefetch their next row while finishing the current one.
+// rows (LDS across wavefronts).  The grid gives every workgroup at least
+// RMS_FWD_WG_BYTES of x (one row block for rows of 8 KB and more, a few
+// blocks for narrow rows); workgroups that get more than one block prefetch
+// the next while finishing the current one.
 #include "common.hpp"
 #include "launch.hpp"
 
+// Grid size: ceil(bytes of x / RMS_FWD_WG_BYTES), at least RMS_FWD_MIN_GRID
+// and at most one workgroup per row block (measured: one block per workgroup
+// is best for rows of 8 KB and more, e.g. 87 vs 92 us for the bf16 residual
+// forward at 16384 x 4096; two 4 KB blocks per workgroup for 128-wide rows).
+#ifndef RMS_FWD_WG_BYTES
+#define RMS_FWD_WG_BYTES 8192
+#endif
+#ifndef RMS_FWD_MIN_GRID
+#define RMS_FWD_MIN_GRID 2048
+#endif
 #ifndef RMS_FWD_MAX_GRID
-#define RMS_FWD_MAX_GRID (256 * 16)
+#define RMS_FWD_MAX_GRID (1 << 20)
 #endif
 // Streaming (nontemporal) access to the row tensors: x/res loads, y/h
 // stores.  Measured best: stores only for the plain forward, loads and
@@ -166,7 +178,11 @@ static hipError_t launch_cfg(const FwdArgs& a, bool residual, hipStream_t s) {
     constexpr int WG = TEAM > 256 ? TEAM : 256;
     constexpr int R = WG / TEAM;
     const int64_t nrb = (a.rows + R - 1) / R;
-    const int grid = (int)(nrb < RMS_FWD_MAX_GRID ? nrb : RMS_FWD_MAX_GRID);
+    const int64_t xbytes = a.rows * (int64_t)a.H * (int64_t)sizeof(T);
+    int64_t want = (xbytes + RMS_FWD_WG_BYTES - 1) / RMS_FWD_WG_BYTES;
+    if (want < RMS_FWD_MIN_GRID) want = RMS_FWD_MIN_GRID;
+    if (want > RMS_FWD_MAX_GRID) want = RMS_FWD_MAX_GRID;
+    const int grid = (int)(nrb < want ? nrb : want);
     if (residual) {
         hipLaunchKernelGGL((fwd_kernel<T, VEC, TEAM, NCH, WG, true>), dim3(grid), dim3(WG), 0, s,
                            (const T*)a.x, (const T*)a.res, (const T*)a.w, (T*)a.h, (T*)a.y, a.rstd,
