@@ -114,3 +114,67 @@ def test_workload_decode_splitrow(splits):
     assert_rstd(f64(rstd), ro)
     # Split and unsplit agree to within one bf16 ulp of each other.
     assert np.max(np.abs(f64(y) - f64(y_plain))) <= np.max(np.abs(yo)) * 2.0 ** -7
+
+
+def test_beyond_2_31_elements():
+    """Tensors of 2^31 + 12288 bf16 elements (524291 rows of 4096): every
+    offset past 2^31 elements (2^32 bytes) must reach its own row.  The input
+    is a seeded block of 4099 rows tiled on the device; 524288 rows (2^31
+    elements) is not a multiple of 4099, so an index that wrapped would read a
+    row holding other values.  The block's outputs are checked against the
+    oracle, and every row of the large run must equal its block row bitwise
+    (row outputs do not depend on the rest of the batch); dw is checked
+    against the oracle with dy scaled by each block row's repeat count (dw is
+    linear in dy)."""
+    P, H, rows = 4099, 4096, (1 << 19) + 3
+    dt = synth.BF16
+    wl = synth.small_case(P, H, dt, seed=31, residual=True)
+    x, w, dy, res = wl.x(), wl.w(), wl.dy(), wl.res()
+    print(f"[full] beyond 2^31 elements: rows={rows} H={H} bf16 (block of {P} rows)", flush=True)
+    xs, ws_, dys, rs_ = to_dev(x, dt), to_dev(w, dt), to_dev(dy, dt), to_dev(res, dt)
+    reps = (rows + P - 1) // P
+
+    def tile(t):
+        return t.repeat(reps, 1)[:rows].contiguous()
+
+    def run(xd, dyd, rd, n):
+        y = torch.empty((n, H), dtype=torch.bfloat16, device=DEV)
+        rstd = torch.empty(n, device=DEV)
+        dx = torch.empty((n, H), dtype=torch.bfloat16, device=DEV)
+        dw = torch.empty(H, dtype=torch.bfloat16, device=DEV)
+        B.rmsnorm_fwd(xd, ws_, y, rstd, wl.eps)
+        B.rmsnorm_bwd(dyd, xd, ws_, rstd, None, dx, dw, _ws(n, H, dt), wl.eps)
+        h = torch.empty((n, H), dtype=torch.bfloat16, device=DEV)
+        yr = torch.empty((n, H), dtype=torch.bfloat16, device=DEV)
+        rr = torch.empty(n, device=DEV)
+        B.rmsnorm_residual_fwd(xd, rd, ws_, h, yr, rr, wl.eps)
+        torch.cuda.synchronize()
+        return y, rstd, dx, dw, h, yr, rr
+
+    small = run(xs, dys, rs_, P)
+    x64, w64, dy64 = (synth.to_f64(a, dt) for a in (x, w, dy))
+    yo, ro = oracle.rmsnorm_fwd(x64, w64, wl.eps)
+    assert_output("y", f64(small[0]), yo, dt)
+    assert_rstd(f64(small[1]), ro)
+    rs = f64(small[1])
+    dxo, _ = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=rs)
+    assert_output("dx", f64(small[2]), dxo, dt)
+    ho, _, _ = oracle.rmsnorm_residual_fwd(x64, synth.to_f64(res, dt), w64, wl.eps, oracle.H_BF16)
+    assert np.array_equal(f64(small[4]), ho), "h must be bit-exact"
+
+    xb, dyb, rb = tile(xs), tile(dys), tile(rs_)
+    assert xb.numel() > (1 << 31)
+    big = run(xb, dyb, rb, rows)
+    del xb, dyb, rb
+    full = (rows // P) * P
+    for name, b, s in zip(("y", "rstd", "dx", "dw", "h", "y(res)", "rstd(res)"), big, small):
+        if name == "dw":
+            continue
+        bb = b[:full].reshape(rows // P, P, *b.shape[1:])
+        assert torch.equal(bb, s.unsqueeze(0).expand_as(bb)), f"{name}: rows differ from the block"
+        assert torch.equal(b[full:], s[:rows - full]), f"{name}: tail rows differ from the block"
+    count = np.full(P, rows // P, dtype=np.float64)
+    count[:rows - full] += 1
+    _, dwo = oracle.rmsnorm_bwd(dy64 * count[:, None], x64, w64, wl.eps, rstd=rs)
+    e_dw = assert_dw(f64(big[3]), dwo, dt)
+    print(f"[full] beyond 2^31 elements: rows match the block bitwise, dw {e_dw:.3g}", flush=True)
