@@ -75,15 +75,6 @@ __device__ __forceinline__ Pack<T, VEC> load_pack(const T* p) {
     return r;
 }
 
-// Make a packed register opaque to the optimiser: values unpacked from it
-// before this point are not reused after it, so the compiler re-derives them
-// (a shift or a mask per element) instead of keeping the float copies live
-// across a reduction.  Emits no instruction.
-template <typename T, int VEC>
-__device__ __forceinline__ void opaque(Pack<T, VEC>& p) {
-    if constexpr (VEC > 1) asm volatile("" : "+v"(p.v));
-}
-
 template <typename T, int VEC>
 __device__ __forceinline__ Pack<T, VEC> zero_pack() {
     Pack<T, VEC> r;
@@ -244,6 +235,30 @@ __device__ __forceinline__ V team_sum(V v, V* lds) {
 #pragma unroll
         for (int k = 1; k < NW; ++k) s += slot[k];
         __syncthreads();  // slots may be reused by the next reduction
+        return s;
+    }
+}
+
+// As team_sum, with one barrier instead of two: the caller alternates
+// between two disjoint slot sets `lds` on successive calls, so a set is only
+// rewritten after every thread has passed the barrier of the call in between
+// (which follows its reads of that set).  Contains __syncthreads() when
+// TEAM > 64.
+template <int TEAM, typename V>
+__device__ __forceinline__ V team_sum_alt(V v, V* lds) {
+    if constexpr (TEAM <= 64) {
+        return team_sum_wave<TEAM>(v);
+    } else {
+        constexpr int NW = TEAM / kWave;
+        v = team_sum_wave<64>(v);
+        const int lt = threadIdx.x % TEAM;
+        const int team = threadIdx.x / TEAM;
+        V* slot = lds + team * NW;
+        if ((lt & (kWave - 1)) == 0) slot[lt / kWave] = v;
+        __syncthreads();
+        V s = slot[0];
+#pragma unroll
+        for (int k = 1; k < NW; ++k) s += slot[k];
         return s;
     }
 }

@@ -42,11 +42,8 @@
 #ifndef RMS_DRES_NT_STORE
 #define RMS_DRES_NT_STORE 1
 #endif
-// Smallest team of the register-trimmed, two-workgroups-per-CU tiles.
-#ifndef RMS_BWD_LEAN_MIN
-#define RMS_BWD_LEAN_MIN 512
-#endif
-// Row blocks in flight per workgroup beyond the one being finished (1 or 2).
+// 1: the next row block loads while the current one is finished (two
+// register sets in turn); 0: one block at a time.
 #ifndef RMS_BWD_PREFETCH
 #define RMS_BWD_PREFETCH 1
 #endif
@@ -71,20 +68,17 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     // Register budget: w cached and the next rows prefetched unless the
     // per-lane tile is large for this workgroup size.
     constexpr bool kCacheW = EB * WG <= 16384;
-    constexpr bool kPrefetch = EB * WG <= 16384;
+    constexpr bool kPrefetch = RMS_BWD_PREFETCH != 0 && EB * WG <= 16384;
     constexpr bool kNtLoad = DRES ? RMS_DRES_NT_LOAD != 0 : RMS_BWD_NT_LOAD != 0;
     constexpr bool kNtStore = DRES ? RMS_DRES_NT_STORE != 0 : RMS_BWD_NT_STORE != 0;
-    constexpr int kDepth = kPrefetch ? RMS_BWD_PREFETCH : 0;
-    // 512-lane tiles re-derive the unpacked row in pass B instead of keeping
-    // it live across the row reduction; that fits two workgroups per CU (the
-    // plain backward stays within 128 VGPRs), which bwd_groups() then uses.
-    // Elsewhere keeping the floats live measured faster.
-    constexpr bool kLean = TEAM >= RMS_BWD_LEAN_MIN && TEAM <= 512;
     // Teams combine their dw sums either side by side ([R][HT], summed per
     // column in team order) when that fits in 32 KiB, or one after another
     // into a single [HT] row.
     constexpr bool kWideComb = R > 1 && R * HT <= 8192;
-    __shared__ double red[TEAM > kWave ? 2 * R * NWT : 1];
+    // Row-sum slots: two sets used in turn (one barrier per sum), each
+    // with room for c and, when recomputing r, sum x^2.
+    constexpr int kRedSet = 2 * R * NWT;
+    __shared__ double red[TEAM > kWave ? 2 * kRedSet : 1];
     __shared__ __align__(16) float comb[R == 1 ? 1 : (kWideComb ? R * HT : HT)];
 
     const int tid = threadIdx.x;
@@ -122,56 +116,54 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
         }
     };
 
-    struct RowRegs {
+    // One row block's operands.  Loads are issued without branches: lanes
+    // outside the tensor (rows past the end, columns past H) read the first
+    // bytes of this workgroup's own partial row instead (one line per
+    // wavefront; the partial row is written only by this workgroup, at the
+    // end) and are masked where the values are used.  With the same number
+    // of loads on every path the compiler waits for exactly the block it is
+    // about to use while the next block's loads stay in flight.
+    struct Blk {
         Pack<T, VEC> x[NCH], dy[NCH], dr[DRES ? NCH : 1];
         float rs;
     };
-    auto load_row = [&](int64_t base, RowRegs& q) {
-        const int64_t row = base + team;
+    const float* dummyf = partial + (int64_t)blockIdx.x * ldp;
+    const T* dummy = reinterpret_cast<const T*>(dummyf);
+    auto issue = [&](int64_t b, Blk& q) {
+        const int64_t row = b + team;
         const bool active = row < end;
         const int64_t off = row * (int64_t)H;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int col = (c * TEAM + lt) * VEC;
             const bool ok = active && col < H;
-            q.x[c] = ok ? load_pack<T, VEC, kNtLoad>(x + off + col) : zero_pack<T, VEC>();
-            q.dy[c] = ok ? load_pack<T, VEC, kNtLoad>(dy + off + col) : zero_pack<T, VEC>();
-            if constexpr (DRES)
-                q.dr[c] = ok ? load_pack<T, VEC, kNtLoad>(dres + off + col) : zero_pack<T, VEC>();
+            q.x[c] = load_pack<T, VEC, kNtLoad>(ok ? x + off + col : dummy);
+            q.dy[c] = load_pack<T, VEC, kNtLoad>(ok ? dy + off + col : dummy);
+            if constexpr (DRES) q.dr[c] = load_pack<T, VEC, kNtLoad>(ok ? dres + off + col : dummy);
         }
-        q.rs = (active && has_rstd) ? rstd[row] : 0.f;
+        q.rs = *((has_rstd && active) ? rstd + row : dummyf);
     };
 
-    // Ring of row blocks in flight: cur is being finished, ahead[d] is the
-    // block d + 1 strides further on (loaded kDepth blocks ahead).
-    RowRegs cur;
-    RowRegs ahead[kDepth > 0 ? kDepth : 1];
-    int64_t base = begin;
-    if constexpr (kDepth > 0) {
-        if (base < end) load_row(base, cur);
-#pragma unroll
-        for (int d = 0; d + 1 < kDepth; ++d)
-            if (base + (d + 1) * stride < end) load_row(base + (d + 1) * stride, ahead[d]);
-    }
-    while (base < end) {
-        const int64_t nb = base + stride;
-        if constexpr (kDepth > 0) {
-            const int64_t fb = base + kDepth * stride;
-            if (fb < end) load_row(fb, ahead[kDepth - 1]);
-        } else {
-            load_row(base, cur);
-        }
-
-        const int64_t row = base + team;
+    auto process = [&](int64_t b, Blk& q, int set) {
+        const int64_t row = b + team;
         const bool active = row < end;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int col = (c * TEAM + lt) * VEC;
+            if (!(active && col < H)) {
+                q.x[c] = zero_pack<T, VEC>();
+                q.dy[c] = zero_pack<T, VEC>();
+                if constexpr (DRES) q.dr[c] = zero_pack<T, VEC>();
+            }
+        }
         // Pass A: row sums.  Values are unpacked again in pass B rather than
         // kept live across the reduction (unpacking is a shift or a mask).
         double cs = 0.0, ss = 0.0;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             float xv[VEC], dyv[VEC], wc[VEC];
-            unpack(cur.x[c], xv);
-            unpack(cur.dy[c], dyv);
+            unpack(q.x[c], xv);
+            unpack(q.dy[c], dyv);
             weights(c, wc);
 #pragma unroll
             for (int k = 0; k < VEC; ++k) {
@@ -179,38 +171,33 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
                 if (!has_rstd) ss += sq64(xv[k], (T*)nullptr);
             }
         }
-        if constexpr (kLean) {
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                opaque(cur.x[c]);
-                opaque(cur.dy[c]);
-            }
-        }
-        cs = team_sum<TEAM>(cs, red);
+        double* rs_slots = red + (TEAM > kWave ? set * kRedSet : 0);
+        cs = team_sum_alt<TEAM>(cs, rs_slots);
         double r;
         if (has_rstd) {
-            r = (double)cur.rs;
+            r = (double)q.rs;
         } else {
-            ss = team_sum<TEAM>(ss, red + R * NWT);
+            ss = team_sum_alt<TEAM>(ss, rs_slots + R * NWT);
             r = rsqrt_f64(ss * inv_h + (double)eps);
         }
         const float rf = (float)r;
         const double kk = r * r * (cs * inv_h);
         const float k_hi = (float)kk;
         const float k_lo = (float)(kk - (double)k_hi);
-        // Pass B: dx and the dw column sums.
+        // Pass B: dx and the dw column sums (masked lanes hold zeros, so
+        // they add nothing to the sums).
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             float xv[VEC], dyv[VEC], wc[VEC], o[VEC];
-            unpack(cur.x[c], xv);
-            unpack(cur.dy[c], dyv);
+            unpack(q.x[c], xv);
+            unpack(q.dy[c], dyv);
             weights(c, wc);
             if constexpr (DRES || sizeof(T) == 4) {
                 // fp64 form: w*dy (exact in fp64), r*(wdy - x k) [+ dres] with
                 // one final rounding.  Used when dx can cancel against dres,
                 // and for fp32 inputs, whose w*dy is not exact in fp32.
                 float drv[VEC];
-                if constexpr (DRES) unpack(cur.dr[c], drv);
+                if constexpr (DRES) unpack(q.dr[c], drv);
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) {
                     const double wdy = (double)wc[k] * (double)dyv[k];
@@ -235,15 +222,44 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
             const int col = (c * TEAM + lt) * VEC;
             if (active && col < H) store_vec<T, VEC, kNtStore>(dx + row * (int64_t)H + col, o);
         }
+    };
 
-        if constexpr (kDepth > 0) {
-            cur = ahead[0];
-#pragma unroll
-            for (int d = 0; d + 1 < kDepth; ++d) ahead[d] = ahead[d + 1];
+    if constexpr (kPrefetch) {
+        // Two register sets in turn: block b + stride loads while block b is
+        // finished.  The last one or two blocks are peeled off the loop so
+        // that nothing is loaded past the workgroup's last block.
+        const int64_t nb = begin < end ? (end - begin + stride - 1) / stride : 0;
+        Blk A, B;
+        int64_t b = begin;
+        if (nb > 0) {
+            issue(b, A);
+            int64_t left = nb;
+            while (left > 2) {
+                issue(b + stride, B);
+                process(b, A, 0);
+                b += stride;
+                issue(b + stride, A);
+                process(b, B, 1);
+                b += stride;
+                left -= 2;
+            }
+            if (left == 2) {
+                issue(b + stride, B);
+                process(b, A, 0);
+                process(b + stride, B, 1);
+            } else {
+                process(b, A, 0);
+            }
         }
-        base = nb;
+    } else {
+        Blk A;
+        int set = 0;
+        for (int64_t b = begin; b < end; b += stride) {
+            issue(b, A);
+            process(b, A, set);
+            set ^= 1;
+        }
     }
-
     // One partial row per workgroup: combine the R teams in team order.
     // With VEC > 1, H is a multiple of VEC, so groups of four columns that
     // start below H end below H (and below HT); ldp is a multiple of 64.
@@ -384,17 +400,13 @@ __global__ __launch_bounds__(kRedWG) void dw_reduce_kernel(const float* __restri
 #define RMS_BWD_MIN_ROWS_PER_GROUP 4
 #endif
 
-int bwd_groups(int64_t rows, int64_t H, DType dt) {
+int bwd_groups(int64_t rows, int64_t H, DType) {
+    // One workgroup per CU on every tile (a pure function of the shape, so
+    // the reduction order and the bits of dw depend on nothing else).
+    (void)H;
     if (rows <= 0) return 0;
-    // The tile of the 128-bit path decides the cap (also when a call falls
-    // back to scalar accesses, so the group count depends on the shape only):
-    // 512-lane tiles run two workgroups per CU, the others one.
-    Geometry g;
-    const int vec = dt == DType::F32 ? 4 : 8;
-    const bool lean = choose_geometry(H, vec, &g) && g.team >= RMS_BWD_LEAN_MIN && g.team <= 512;
-    const int64_t cap = lean ? 2 * RMS_BWD_MAX_GROUPS : RMS_BWD_MAX_GROUPS;
     const int64_t n = (rows + RMS_BWD_MIN_ROWS_PER_GROUP - 1) / RMS_BWD_MIN_ROWS_PER_GROUP;
-    return (int)(n < cap ? n : cap);
+    return (int)(n < RMS_BWD_MAX_GROUPS ? n : RMS_BWD_MAX_GROUPS);
 }
 
 int partial_ld(int64_t H) { return (int)((H + 63) / 64 * 64); }

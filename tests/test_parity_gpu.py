@@ -98,6 +98,37 @@ def test_bwd(rows, H, dtype, mode):
     assert_dw(f64(dw), dwo, dtype)
 
 
+# Row counts that give the backward's 256 workgroups several row blocks each,
+# unequal between workgroups, with a partly filled last block: the loop that
+# alternates two register sets and its peeled last one or two blocks (and the
+# tiles that load one block at a time).  Rows per block: 2 (bf16 H = 4096),
+# 64 (bf16 H = 128), 1 (bf16 H = 8192), 4 (fp32 H = 896), 1 (bf16 H = 16384).
+MULTI_BLOCK = [(synth.BF16, 1026, 4096), (synth.BF16, 1539, 4096), (synth.BF16, 2559, 4096),
+               (synth.BF16, 32868, 128), (synth.BF16, 775, 8192), (synth.F32, 2053, 896),
+               (synth.BF16, 513, 16384)]
+
+
+@pytest.mark.parametrize("mode", ["saved_rstd", "recompute", "dres"])
+@pytest.mark.parametrize("dtype,rows,H", MULTI_BLOCK)
+def test_bwd_multi_block(dtype, rows, H, mode):
+    wl, x, w, dy, _, dres = _inputs(rows, H, dtype, seed=11 * rows + H, outliers=0.01)
+    x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
+    _, r64 = oracle.rmsnorm_fwd(x64, w64, wl.eps)
+    rstd32 = round_f32(r64)
+    xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
+    rstd_d = torch.from_numpy(rstd32.astype(np.float32)).to(DEV) if mode != "recompute" else None
+    dres_d = to_dev(dres, dtype) if mode == "dres" else None
+    dx = _empty(rows, H, dtype)
+    dw = torch.full((H,), float("nan"), dtype=torch_dtype(dtype), device=DEV)
+    B.rmsnorm_bwd(dyd, xd, wd, rstd_d, dres_d, dx, dw, _ws(rows, H, dtype), wl.eps)
+    torch.cuda.synchronize()
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps,
+                                  rstd=None if mode == "recompute" else rstd32,
+                                  dres=synth.to_f64(dres, dtype) if mode == "dres" else None)
+    assert_output("dx", f64(dx), dxo, dtype)
+    assert_dw(f64(dw), dwo, dtype)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("rows,H", [(64, 896), (33, 4096), (300, 128), (9, 8192)])
 def test_chain_fwd_then_bwd(rows, H, dtype):
