@@ -515,6 +515,48 @@ def suite(path, reps=30, warmup=20):
             f.write(json.dumps(d) + "\n")
 
 
+# ---------------------------------------------------------------- counter passes
+
+COUNTER_WORKLOADS = ["c1_f32_64x896", "c2_bf16_4096x4096", "c5a_bf16_262144x128",
+                     "c5b_bf16_8192x8192", "c4_bf16_residual_16384x4096", "c3_bf16_decode_1x896"]
+
+
+def counters_pass(n):
+    """Every workload's kernels, n launches each on rotating buffer sets, with
+    no timing: the program that rocprofv3 counter passes run over.  Per
+    workload, in COUNTER_WORKLOADS order, each repetition launches forward,
+    backward row pass and dw reduce (residual forward and the row pass with
+    dres for the residual workload; the one-row forward and the split-row
+    forward with 4 splits for decode), so every dw reduce dispatch follows the
+    row pass of its own workload."""
+    import torch
+    from bwd_rmsnorm_fwd_amd import synth
+
+    stream = torch.cuda.current_stream()
+    for name in COUNTER_WORKLOADS:
+        wl = synth.WORKLOADS[name]
+        residual = name.startswith("c4")
+        sets = Sets(wl, k=1 if wl.rows == 1 else None, residual=residual, dres=residual)
+        C = Calls(sets, stream)
+        partials = torch.empty(4, dtype=torch.float32, device="cuda")
+        for i in range(n):
+            s = sets.sets[i % sets.k]
+            if wl.rows == 1:
+                run(C.fwd(s))
+                run(C.splitrow(s, partials, 4))
+            elif residual:
+                run(C.residual_fwd(s))
+                run(C.bwd_rows(s, x_key="h", dres=True))
+                run(C.dw_reduce(s))
+            else:
+                run(C.fwd(s))
+                run(C.bwd_rows(s))
+                run(C.dw_reduce(s))
+        torch.cuda.synchronize()
+        del sets, C
+        torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- entry
 
 def main():
@@ -531,6 +573,9 @@ def main():
     ap.add_argument("--copy-ref-mb", type=int, default=0,
                     help="after the step, run a plain device copy of this many MiB (reference "
                          "kernel of known size for scaling rocprofv3 byte counters)")
+    ap.add_argument("--counters-pass", type=int, default=0, metavar="N",
+                    help="instead of timing, launch every workload's kernels N times each "
+                         "(the program for rocprofv3 counter passes), then the --copy-ref-mb copy")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -542,6 +587,12 @@ def main():
 
     import torch
     torch.cuda.init()
+    if args.counters_pass:
+        counters_pass(args.counters_pass)
+        copy_ref(args.copy_ref_mb)
+        print(json.dumps({"counters_pass": args.counters_pass, "workloads": COUNTER_WORKLOADS,
+                          "copy_ref_bytes": args.copy_ref_mb << 20}), flush=True)
+        return
     r = bench_step(args.steps, args.warmup)
     wl = r["wl"]
     total_bytes = r["fwd_bytes"] + r["bwd_bytes"]
@@ -590,14 +641,22 @@ def main():
     if args.suite:
         suite(args.suite)
     if args.copy_ref_mb:
-        n = args.copy_ref_mb << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        line["copy_ref_bytes"] = n
+        copy_ref(args.copy_ref_mb)
+        line["copy_ref_bytes"] = args.copy_ref_mb << 20
     print(json.dumps(line), flush=True)
+
+
+def copy_ref(mb):
+    """A plain device copy of `mb` MiB, three times: a kernel of known size
+    whose counters scale the byte counters of the others."""
+    if not mb:
+        return
+    import torch
+    src = torch.ones(mb << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
