@@ -21,7 +21,11 @@ struct Geometry {
 };
 
 // Returns false when H needs more than the largest register tile.
-bool choose_geometry(int64_t H, int vec, Geometry* g);
+// `wide` selects the tile for the kinds that stream more row tensors (the
+// residual forward, the backward with a residual-stream gradient): one
+// 16-byte chunk per lane on a 512-lane team where the others use two chunks
+// on 256 lanes.
+bool choose_geometry(int64_t H, int vec, bool wide, Geometry* g);
 
 // Largest vector width usable for these pointers and H (elements; 16 bytes
 // worth when everything is aligned, else 1).

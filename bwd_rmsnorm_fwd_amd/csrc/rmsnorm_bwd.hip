@@ -417,8 +417,9 @@ static hipError_t launch_rows_cfg(const BwdArgs& a, hipStream_t s) {
     // workgroups among several rows, larger tiles use smaller workgroups so
     // that the row, its prefetched successor, w and the dw sums stay in
     // registers.  Teams wider than that fill the workgroup alone.
+    // A one-chunk team of 512 lanes or more is a workgroup of its own.
     constexpr int EB = NCH * VEC * (int)sizeof(T);
-    constexpr int WGD = EB <= 16 ? 1024 : (EB <= 32 ? 512 : 256);
+    constexpr int WGD = (TEAM >= 512 && NCH == 1) ? TEAM : (EB <= 16 ? 1024 : (EB <= 32 ? 512 : 256));
     constexpr int WG = TEAM > WGD ? TEAM : WGD;
     if (a.dres) {
         hipLaunchKernelGGL((bwd_rows_kernel<T, VEC, TEAM, NCH, WG, true>), dim3(a.G), dim3(WG), 0,
@@ -435,11 +436,12 @@ static hipError_t launch_rows_cfg(const BwdArgs& a, hipStream_t s) {
 template <typename T, int VEC>
 static hipError_t dispatch_rows(const BwdArgs& a, hipStream_t s) {
     Geometry g;
-    if (!choose_geometry(a.H, VEC, &g)) return hipErrorInvalidValue;
+    if (!choose_geometry(a.H, VEC, a.dres != nullptr, &g)) return hipErrorInvalidValue;
 #define RMS_CASE(TM, NC) \
     if (g.team == TM && g.nch == NC) return launch_rows_cfg<T, VEC, TM, NC>(a, s);
     RMS_CASE(1, 1) RMS_CASE(2, 1) RMS_CASE(4, 1) RMS_CASE(8, 1) RMS_CASE(16, 1) RMS_CASE(32, 1)
-    RMS_CASE(64, 1) RMS_CASE(64, 2) RMS_CASE(128, 2) RMS_CASE(256, 2) RMS_CASE(512, 2)
+    RMS_CASE(64, 1) RMS_CASE(64, 2) RMS_CASE(128, 2) RMS_CASE(256, 2) RMS_CASE(512, 1)
+    RMS_CASE(512, 2)
     RMS_CASE(1024, 2) RMS_CASE(1024, 4) RMS_CASE(1024, 8) RMS_CASE(1024, 16)
 #undef RMS_CASE
     return hipErrorInvalidValue;

@@ -198,11 +198,12 @@ static hipError_t launch_cfg(const FwdArgs& a, bool residual, hipStream_t s) {
 template <typename T, int VEC>
 static hipError_t dispatch(const FwdArgs& a, bool residual, hipStream_t s) {
     Geometry g;
-    if (!choose_geometry(a.H, VEC, &g)) return hipErrorInvalidValue;
+    if (!choose_geometry(a.H, VEC, residual, &g)) return hipErrorInvalidValue;
 #define RMS_CASE(TM, NC) \
     if (g.team == TM && g.nch == NC) return launch_cfg<T, VEC, TM, NC>(a, residual, s);
     RMS_CASE(1, 1) RMS_CASE(2, 1) RMS_CASE(4, 1) RMS_CASE(8, 1) RMS_CASE(16, 1) RMS_CASE(32, 1)
-    RMS_CASE(64, 1) RMS_CASE(64, 2) RMS_CASE(128, 2) RMS_CASE(256, 2) RMS_CASE(512, 2)
+    RMS_CASE(64, 1) RMS_CASE(64, 2) RMS_CASE(128, 2) RMS_CASE(256, 2) RMS_CASE(512, 1)
+    RMS_CASE(512, 2)
     RMS_CASE(1024, 2) RMS_CASE(1024, 4) RMS_CASE(1024, 8) RMS_CASE(1024, 16)
 #undef RMS_CASE
     return hipErrorInvalidValue;
