@@ -248,18 +248,23 @@ def test_guard_bands_untouched():
     assert not torch.isnan(rstd).any()
 
 
-@pytest.mark.parametrize("dtype", DTYPES)
-def test_deterministic(dtype):
-    """Fixed reduction order: repeated calls give bitwise-identical results."""
-    rows, H = 1000, 4096
-    wl, x, w, dy, *_ = _inputs(rows, H, dtype, seed=1)
+@pytest.mark.parametrize("dtype,rows,H,mode", [
+    (synth.BF16, 1000, 4096, "saved_rstd"), (synth.F32, 1000, 4096, "saved_rstd"),
+    (synth.BF16, 2559, 4096, "dres"), (synth.BF16, 2559, 4096, "recompute"),
+    (synth.BF16, 775, 8192, "saved_rstd"), (synth.BF16, 32868, 128, "dres")])
+def test_deterministic(dtype, rows, H, mode):
+    """Fixed reduction order: repeated calls give bitwise-identical results
+    (shapes with one to five row blocks per workgroup, each backward kind)."""
+    wl, x, w, dy, _, dres = _inputs(rows, H, dtype, seed=1)
     xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
+    drd = to_dev(dres, dtype) if mode == "dres" else None
     outs = []
     for _ in range(3):
         y, rstd = _empty(rows, H, dtype), torch.empty(rows, device=DEV)
         dx, dw = _empty(rows, H, dtype), torch.empty(H, dtype=torch_dtype(dtype), device=DEV)
         B.rmsnorm_fwd(xd, wd, y, rstd, wl.eps)
-        B.rmsnorm_bwd(dyd, xd, wd, rstd, None, dx, dw, _ws(rows, H, dtype), wl.eps)
+        B.rmsnorm_bwd(dyd, xd, wd, None if mode == "recompute" else rstd, drd, dx, dw,
+                      _ws(rows, H, dtype), wl.eps)
         torch.cuda.synchronize()
         outs.append([t.view(torch.int16 if t.element_size() == 2 else torch.int32).cpu()
                      for t in (y, rstd, dx, dw)])
@@ -298,11 +303,13 @@ def test_errors_are_reported():
     assert e.value.status == B.EWORKSPACE
 
 
-def test_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("rows,H", [(300, 896), (1539, 4096)])
+def test_graph_capture_replays_match_eager(rows, H):
     """Every entry point records into a HIP graph (no allocation, no sync, no
     memset inside); replays, with eager work and synchronisation in between,
-    reproduce the eager results bit for bit."""
-    rows, H, dtype = 300, 896, synth.BF16
+    reproduce the eager results bit for bit (one row block per backward
+    workgroup, and three to four)."""
+    dtype = synth.BF16
     wl, x, w, dy, res, dres = _inputs(rows, H, dtype, seed=77)
     xd, wd, dyd, rd, drd = (to_dev(a, dtype) for a in (x, w, dy, res, dres))
     td = torch.bfloat16
