@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 # (rows, H): tails of every team width, several tiles, vector and scalar paths.
 SHAPES = [(1, 1), (3, 2), (5, 7), (64, 8), (65, 16), (33, 120), (257, 128), (17, 129),
           (9, 256), (7, 500), (70, 512), (11, 895), (64, 896), (5, 897), (6, 1024),
-          (4, 2040), (3, 2048), (5, 4095), (7, 4096), (3, 5000), (2, 8192), (2, 16384)]
+          (4, 2040), (3, 2048), (6, 1500), (9, 3000), (5, 4095), (7, 4096), (3, 5000), (2, 8192),
+          (2, 16384)]
 DTYPES = [synth.BF16, synth.F32]
 
 
