@@ -130,6 +130,59 @@ def test_bwd_multi_block(dtype, rows, H, mode):
     assert_dw(f64(dw), dwo, dtype)
 
 
+def _random_case(k):
+    """Seeded draw of a shape and kind: H across every tile class (and odd
+    widths, which take the scalar path), rows from one to a few hundred."""
+    rng = np.random.default_rng(9000 + k)
+    dtype = DTYPES[k % 2]
+    H = int(rng.choice([int(rng.integers(1, 130)), int(rng.integers(130, 1100)),
+                        int(rng.integers(1100, 4200)), int(rng.integers(4200, 16385))]))
+    if rng.random() < 0.6:          # mostly widths that allow 128-bit accesses
+        H = max(8, H // 8 * 8)
+    rows = int(rng.integers(1, max(2, min(400, 2_000_000 // H))))
+    mode = ["saved_rstd", "recompute", "dres"][k % 3]
+    return dtype, rows, H, mode
+
+
+@pytest.mark.parametrize("k", range(60))
+def test_random_shapes(k):
+    """Forward (plain or residual) and backward on seeded random shapes,
+    element by element against the oracle."""
+    dtype, rows, H, mode = _random_case(k)
+    wl, x, w, dy, res, dres = _inputs(rows, H, dtype, seed=100 + k, outliers=0.01)
+    x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
+    xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
+    rstd = torch.full((rows,), float("nan"), device=DEV)
+    if mode == "dres":
+        rd = to_dev(res, dtype)
+        h, y = _empty(rows, H, dtype), _empty(rows, H, dtype)
+        B.rmsnorm_residual_fwd(xd, rd, wd, h, y, rstd, wl.eps)
+        kind = oracle.H_BF16 if dtype == synth.BF16 else oracle.H_F32
+        ho, yo, ro = oracle.rmsnorm_residual_fwd(x64, synth.to_f64(res, dtype), w64, wl.eps, kind)
+        torch.cuda.synchronize()
+        assert np.array_equal(f64(h), ho), "h must be bit-exact"
+        xin, xin64 = h, ho
+    else:
+        y = _empty(rows, H, dtype)
+        B.rmsnorm_fwd(xd, wd, y, rstd, wl.eps)
+        yo, ro = oracle.rmsnorm_fwd(x64, w64, wl.eps)
+        xin, xin64 = xd, x64
+    torch.cuda.synchronize()
+    assert_output("y", f64(y), yo, dtype)
+    assert_rstd(f64(rstd), ro)
+    dres_d = to_dev(dres, dtype) if mode == "dres" else None
+    dx = _empty(rows, H, dtype)
+    dw = torch.full((H,), float("nan"), dtype=torch_dtype(dtype), device=DEV)
+    B.rmsnorm_bwd(dyd, xin, wd, None if mode == "recompute" else rstd, dres_d, dx, dw,
+                  _ws(rows, H, dtype), wl.eps)
+    torch.cuda.synchronize()
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, xin64, w64, wl.eps,
+                                  rstd=None if mode == "recompute" else f64(rstd),
+                                  dres=synth.to_f64(dres, dtype) if mode == "dres" else None)
+    assert_output("dx", f64(dx), dxo, dtype)
+    assert_dw(f64(dw), dwo, dtype)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("rows,H", [(64, 896), (33, 4096), (300, 128), (9, 8192)])
 def test_chain_fwd_then_bwd(rows, H, dtype):
