@@ -38,24 +38,30 @@ H_EXACT = 2
 _lib = None
 
 
-def build() -> str:
+def build(src: str = _SRC, out: str = _LIB) -> str:
     """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
     cmd = [
         "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-        "-fno-fast-math", "-o", _LIB + ".tmp", _SRC, "-lm",
+        "-fno-fast-math", "-o", out + ".tmp", src, "-lm",
     ]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    # RMSNORM_ORACLE_LIB names another build of this source to load instead;
+    # the mutation test uses it to run the pins against deliberately broken
+    # copies of the oracle.
+    path = os.environ.get("RMSNORM_ORACLE_LIB")
+    if not path:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+    lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     i64 = ctypes.c_int64
     lib.oracle_round_bf16.argtypes = [ctypes.c_double]
