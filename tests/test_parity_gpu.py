@@ -9,6 +9,8 @@ test_parity_full_gpu.py.
 Tolerances: fp32 I/O 2e-6 normwise per tensor; bf16 I/O 1 bf16 ulp per element
 on y and dx, bit-exact h, 1e-2 normwise on dw; fp32 rstd 2e-6 relative.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -128,6 +130,62 @@ def test_bwd_multi_block(dtype, rows, H, mode):
                                   dres=synth.to_f64(dres, dtype) if mode == "dres" else None)
     assert_output("dx", f64(dx), dxo, dtype)
     assert_dw(f64(dw), dwo, dtype)
+
+
+def _degenerate_rows(H, dtype):
+    """Rows the method treats specially: all zeros (y = 0, r = 1/sqrt(eps)),
+    constant rows of either sign, a single non-zero element, tiny and large
+    magnitudes (still inside the fp32 range of the squares)."""
+    rng = np.random.default_rng(H)
+    rows = [np.zeros(H), np.full(H, 3.0), np.full(H, -0.5), np.zeros(H),
+            rng.standard_normal(H) * 1e-12, rng.standard_normal(H) * 1e9]
+    rows[3][H // 3] = 5.0
+    return synth.quantise(np.stack(rows).astype(np.float32), dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("H", [128, 896, 4096, 8192])
+def test_degenerate_rows(dtype, H):
+    x = _degenerate_rows(H, dtype)
+    rows = x.shape[0]
+    wl, _, w, dy, *_ = _inputs(rows, H, dtype, seed=H + 3)
+    eps = 1e-6
+    x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
+    xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
+    y, rstd = _empty(rows, H, dtype), torch.full((rows,), float("nan"), device=DEV)
+    dx = _empty(rows, H, dtype)
+    dw = torch.full((H,), float("nan"), dtype=torch_dtype(dtype), device=DEV)
+    B.rmsnorm_fwd(xd, wd, y, rstd, eps)
+    B.rmsnorm_bwd(dyd, xd, wd, rstd, None, dx, dw, _ws(rows, H, dtype), eps)
+    torch.cuda.synchronize()
+    yo, ro = oracle.rmsnorm_fwd(x64, w64, eps)
+    assert_output("y", f64(y), yo, dtype)
+    assert_rstd(f64(rstd), ro)
+    assert np.all(f64(y)[0] == 0.0), "a zero row gives y = 0"
+    assert f64(rstd)[0] == float(np.float32(1.0 / math.sqrt(eps))), "zero row: r = 1/sqrt(eps)"
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, eps, rstd=f64(rstd))
+    assert_output("dx", f64(dx), dxo, dtype)
+    assert_dw(f64(dw), dwo, dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("H", [1, 7, 896, 4096])
+def test_constant_rows_eps0_give_signed_w(dtype, H):
+    """At eps = 0 a constant row x = c (c = +-2^k) has r = 1/|c| exactly and
+    y = sign(c) w bit for bit."""
+    cs = [1.0, -1.0, 8.0, -0.25, 2.0 ** -20, -(2.0 ** 30)]
+    x = np.stack([np.full(H, c) for c in cs])
+    x = synth.quantise(x.astype(np.float32), dtype)
+    rows = len(cs)
+    _, _, w, *_ = _inputs(rows, H, dtype, seed=H + 5)
+    xd, wd = to_dev(x, dtype), to_dev(w, dtype)
+    y, rstd = _empty(rows, H, dtype), torch.empty(rows, device=DEV)
+    B.rmsnorm_fwd(xd, wd, y, rstd, 0.0)
+    torch.cuda.synchronize()
+    w64 = synth.to_f64(w, dtype)
+    for i, c in enumerate(cs):
+        assert f64(rstd)[i] == 1.0 / abs(c), (i, c)
+        assert np.array_equal(f64(y)[i], math.copysign(1.0, c) * w64), (i, c)
 
 
 def _random_case(k):
