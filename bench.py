@@ -162,6 +162,42 @@ class Calls:
                  self.rows, self.H, self.eps, splits, self.code, self.stream))
 
 
+def c_loops():
+    """The host launch-loop helper (bwd_rmsnorm_fwd_amd/bench_loops.cpp), or
+    None when it has not been built."""
+    path = os.path.join(ROOT, "bwd_rmsnorm_fwd_amd", "libbench_loops.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    vp, i64, f32, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    L.bench_fwd_loop.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, f32, i32, vp]
+    L.bench_splitrow_loop.argtypes = [vp, i32, vp, vp, vp, vp, vp, sz, i64, i64, f32, i32, i32, vp]
+    L.bench_gemv_loop.argtypes = [vp, i32, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    for f in (L.bench_fwd_loop, L.bench_splitrow_loop, L.bench_gemv_loop):
+        f.restype = i32
+    return L
+
+
+def time_c_loop(loop, call, ncalls, stream):
+    """µs per call of `call` (fn, args) made `ncalls` times back to back by a
+    loop in C (loop(fn, n, *args)), bracketed by events on `stream`."""
+    import torch
+    fn, args = call
+    fp = ctypes.cast(fn, ctypes.c_void_p)
+    st = loop(fp, 200, *args)
+    if st:
+        raise RuntimeError(f"{fn.__name__}: status {st}")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    st = loop(fp, ncalls, *args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    if st:
+        raise RuntimeError(f"{fn.__name__}: status {st}")
+    return e0.elapsed_time(e1) * 1e3 / ncalls
+
+
 def run(call):
     fn, args = call
     st = fn(*args)
@@ -394,7 +430,9 @@ def suite(path, reps=30, warmup=20):
     del sets, C
     torch.cuda.empty_cache()
 
-    # Decode: 10k back-to-back calls on one stream, µs per call.
+    # Decode: 10k back-to-back calls on one stream, µs per call: from a
+    # Python loop, from a loop in C, and replayed from a HIP graph.
+    CL = c_loops()
     wl = synth.WORKLOADS["c3_bf16_decode_1x896"]
     sets = Sets(wl, k=1)
     C = Calls(sets, stream)
@@ -421,6 +459,13 @@ def suite(path, reps=30, warmup=20):
         emit({"name": f"{wl.name}/{label}", "us_per_call": round(us, 3), "calls": ncalls,
               "launches_per_call": 1 if splits == 0 else 2,
               "bytes": fwd_bytes(1, wl.H, 2), "workload": wl.name})
+        if CL is not None:
+            loop = CL.bench_fwd_loop if splits == 0 else CL.bench_splitrow_loop
+            uc = time_c_loop(loop, call, ncalls, stream)
+            emit({"name": f"{wl.name}/{label}_c_loop", "us_per_call": round(uc, 3),
+                  "calls": ncalls, "launches_per_call": 1 if splits == 0 else 2,
+                  "bytes": fwd_bytes(1, wl.H, 2), "workload": wl.name,
+                  "note": "calls made by a loop in C (no Python per call)"})
         # The same calls captured once in a HIP graph (100 per graph) and
         # replayed: the host launch cost per call disappears.
         per_graph, replays = 100, ncalls // 100
@@ -486,6 +531,12 @@ def suite(path, reps=30, warmup=20):
         emit({"name": f"{gw.name}/gemv_S{splits}", "us_per_call": round(us, 3), "calls": ncalls,
               "launches_per_call": 1 if splits == 1 else 2, "bytes": gbytes,
               "GB_s": round(gbytes / us / 1e3, 1), "workload": gw.name})
+        if CL is not None:
+            uc = time_c_loop(CL.bench_gemv_loop, call, ncalls, stream)
+            emit({"name": f"{gw.name}/gemv_S{splits}_c_loop", "us_per_call": round(uc, 3),
+                  "calls": ncalls, "launches_per_call": 1 if splits == 1 else 2, "bytes": gbytes,
+                  "GB_s": round(gbytes / uc / 1e3, 1), "workload": gw.name,
+                  "note": "calls made by a loop in C (no Python per call)"})
         cs = torch.cuda.Stream()
         cs.wait_stream(stream)
         c2 = gcall(cs)

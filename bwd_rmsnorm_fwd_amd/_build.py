@@ -52,6 +52,22 @@ def build(out_path: str = LIB_PATH, defines=(), build_dir: str | None = None, jo
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out_path)
+    build_bench_loops()
+    return out_path
+
+
+BENCH_LOOPS_SRC = os.path.join(PKG, "bench_loops.cpp")
+BENCH_LOOPS_PATH = os.path.join(PKG, "libbench_loops.so")
+
+
+def build_bench_loops(out_path: str = BENCH_LOOPS_PATH) -> str:
+    """The benchmark's host launch loops (plain host C++, no device code)."""
+    tmp = out_path + ".tmp"
+    cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-shared", "-o", tmp, BENCH_LOOPS_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for bench_loops.cpp:\n{' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, out_path)
     return out_path
 
 
