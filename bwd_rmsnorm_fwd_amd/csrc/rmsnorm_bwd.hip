@@ -180,7 +180,11 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
             ss = team_sum_alt<TEAM>(ss, rs_slots + R * NWT);
             r = rsqrt_f64(ss * inv_h + (double)eps);
         }
-        const float rf = (float)r;
+        // Rows past the end add nothing to dw: their scale is zero, not the
+        // r of zero inputs (infinite at eps = 0) or the value their rstd
+        // lane read from the workspace (whatever the caller's buffer held),
+        // either of which would turn the 0 * r products into NaN.
+        const float rf = active ? (float)r : 0.f;
         const double kk = r * r * (cs * inv_h);
         const float k_hi = (float)kk;
         const float k_lo = (float)(kk - (double)k_hi);

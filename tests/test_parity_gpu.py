@@ -132,6 +132,42 @@ def test_bwd_multi_block(dtype, rows, H, mode):
     assert_dw(f64(dw), dwo, dtype)
 
 
+# The backward's workspace comes from the caller uninitialised.  Whatever it
+# holds (here every float of it NaN, +inf or -inf) must not reach dw, also
+# through the rows past the end of a partly filled last row block; nor may r
+# recomputed at eps = 0, which is infinite for such rows' zero inputs.  Each
+# shape leaves at least one workgroup with a partly filled last block.
+STALE = [(synth.BF16, 300, 128), (synth.BF16, 3, 4096), (synth.BF16, 1539, 4096),
+         (synth.BF16, 33, 896), (synth.F32, 2053, 896), (synth.BF16, 7, 500),
+         (synth.F32, 5, 4095), (synth.BF16, 775, 8192)]
+
+
+@pytest.mark.parametrize("fill", ["nan", "inf", "-inf"])
+@pytest.mark.parametrize("mode", ["saved_rstd", "recompute_eps0", "dres"])
+@pytest.mark.parametrize("dtype,rows,H", STALE)
+def test_bwd_ignores_stale_workspace(dtype, rows, H, mode, fill):
+    eps = 0.0 if mode == "recompute_eps0" else 1e-6
+    wl, x, w, dy, _, dres = _inputs(rows, H, dtype, seed=13 * rows + H)
+    x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
+    _, r64 = oracle.rmsnorm_fwd(x64, w64, eps)
+    rstd32 = round_f32(r64)
+    xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
+    saved = mode != "recompute_eps0"
+    rstd_d = torch.from_numpy(rstd32.astype(np.float32)).to(DEV) if saved else None
+    dres_d = to_dev(dres, dtype) if mode == "dres" else None
+    ws = _ws(rows, H, dtype)
+    ws[: ws.numel() // 4 * 4].view(torch.float32).fill_(float(fill))
+    dx = _empty(rows, H, dtype)
+    dw = torch.full((H,), float("nan"), dtype=torch_dtype(dtype), device=DEV)
+    B.rmsnorm_bwd(dyd, xd, wd, rstd_d, dres_d, dx, dw, ws, eps)
+    torch.cuda.synchronize()
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, eps, rstd=rstd32 if saved else None,
+                                  dres=synth.to_f64(dres, dtype) if mode == "dres" else None)
+    assert np.all(np.isfinite(f64(dw))), "dw picked up a non-finite value"
+    assert_output("dx", f64(dx), dxo, dtype)
+    assert_dw(f64(dw), dwo, dtype)
+
+
 def _degenerate_rows(H, dtype):
     """Rows the method treats specially: all zeros (y = 0, r = 1/sqrt(eps)),
     constant rows of either sign, a single non-zero element, tiny and large
