@@ -62,12 +62,26 @@ template <> struct Pack<bf16_t, 1> { bf16_t v; };
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// Round two floats to bfloat16 (nearest even; gfx950 converts natively) and pack.
+// Round two floats to bfloat16 (nearest even) and pack, a in the low half.
+// Converted as one two-element vector so that it compiles to gfx950's single
+// two-operand v_cvt_pk_bf16_f32 (two scalar conversions compile to two of
+// them, each with one operand, plus a shift and an or).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    __bf16 ha = (__bf16)a;
-    __bf16 hb = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+    const bf16x2_t h = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// The same rounding, one element at a time (two one-operand conversions, a
+// shift and an or).  Kept for the residual backward's fp64 dx, where the
+// single packed conversion led the compiler to chain every element's fp64
+// arithmetic through one register pair (measured 86.0 -> 90.5 us for the
+// bf16 16384 x 4096 row pass with dres); everywhere else the packed form is
+// faster.
+__device__ __forceinline__ uint32_t pack_bf16x2_split(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
 __device__ __forceinline__ float round_to(float v, float*) { return v; }
@@ -115,7 +129,7 @@ __device__ __forceinline__ void unpack(const Pack<T, VEC>& p, float (&f)[VEC]) {
     }
 }
 
-template <typename T, int VEC, bool NT = false>
+template <typename T, int VEC, bool NT = false, bool kSplitCvt = false>
 __device__ __forceinline__ void store_vec(T* p, const float (&f)[VEC]) {
     if constexpr (sizeof(T) == 4 && VEC == 4) {
         st128<NT>(p, u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
@@ -123,6 +137,9 @@ __device__ __forceinline__ void store_vec(T* p, const float (&f)[VEC]) {
     } else if constexpr (sizeof(T) == 4 && VEC == 1) {
         if constexpr (NT) __builtin_nontemporal_store(f[0], reinterpret_cast<float*>(p));
         else *reinterpret_cast<float*>(p) = f[0];
+    } else if constexpr (VEC == 8 && kSplitCvt) {
+        st128<NT>(p, u32x4{pack_bf16x2_split(f[0], f[1]), pack_bf16x2_split(f[2], f[3]),
+                           pack_bf16x2_split(f[4], f[5]), pack_bf16x2_split(f[6], f[7])});
     } else if constexpr (VEC == 8) {
         st128<NT>(p, u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
                        pack_bf16x2(f[6], f[7])});
@@ -170,16 +187,21 @@ constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7-i within 8 lanes
 constexpr int kRowMirror = 0x140;      // lane i <-> 15-i within 16 lanes
 
+// Every control above gives each lane a source lane inside its own 16-lane
+// row, and all rows and banks are enabled, so every lane is written from its
+// source and the instruction's "old" operand is never read: mov_dpp leaves it
+// unspecified, which spares the two zero moves per 64-bit step that an
+// explicit old value costs.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
     int2 p = __builtin_bit_cast(int2, v);
-    p.x = __builtin_amdgcn_update_dpp(0, p.x, CTRL, 0xF, 0xF, false);
-    p.y = __builtin_amdgcn_update_dpp(0, p.y, CTRL, 0xF, 0xF, false);
+    p.x = __builtin_amdgcn_mov_dpp(p.x, CTRL, 0xF, 0xF, false);
+    p.y = __builtin_amdgcn_mov_dpp(p.y, CTRL, 0xF, 0xF, false);
     return __builtin_bit_cast(double, p);
 }
 

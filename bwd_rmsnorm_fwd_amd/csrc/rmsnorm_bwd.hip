@@ -224,7 +224,7 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
                 }
             }
             const int col = (c * TEAM + lt) * VEC;
-            if (active && col < H) store_vec<T, VEC, kNtStore>(dx + row * (int64_t)H + col, o);
+            if (active && col < H) store_vec<T, VEC, kNtStore, DRES>(dx + row * (int64_t)H + col, o);
         }
     };
 
