@@ -150,6 +150,69 @@ __device__ __forceinline__ void store_vec(T* p, const float (&f)[VEC]) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Raw buffer access.  A buffer resource holds a base address and a size in
+// bytes; a load at an offset at or past the size returns zero without
+// reading memory, and a store there is dropped.  Row kernels address a block
+// of rows through resources sized to the rows that exist, and give lanes of
+// columns past H an offset past every size (kBufOutside), so neither needs a
+// branch, a mask or a substitute address.
+constexpr int kBufWord3 = 0x00020000;          // untyped access, 32-bit data format
+constexpr uint32_t kBufOutside = 0x80000000u;  // beyond any resource made here
+// Cache-policy bits of the aux operand (gfx940-family encoding).
+constexpr int kAuxNt = 2;
+constexpr int kAuxSc1 = 16;
+
+typedef __amdgpu_buffer_rsrc_t BufRes;
+
+__device__ __forceinline__ BufRes buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kBufWord3);
+}
+
+template <typename T, int VEC, bool NT = false>
+__device__ __forceinline__ Pack<T, VEC> buf_load_pack(BufRes r, uint32_t off) {
+    constexpr int aux = NT ? kAuxNt : 0;
+    Pack<T, VEC> p;
+    if constexpr (VEC == 1 && sizeof(T) == 2) {
+        p.v = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, aux);
+    } else if constexpr (VEC == 1) {
+        p.v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, aux));
+    } else {
+        p.v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, aux);
+    }
+    return p;
+}
+
+__device__ __forceinline__ float buf_load_f32(BufRes r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+// store_vec through a resource; streaming (NT) stores are nontemporal with
+// device scope, as st128's.
+template <typename T, int VEC, bool NT = false, bool kSplitCvt = false>
+__device__ __forceinline__ void buf_store_vec(BufRes r, uint32_t off, const float (&f)[VEC]) {
+    constexpr int aux = NT ? (kAuxNt | kAuxSc1) : 0;
+    if constexpr (sizeof(T) == 4 && VEC == 4) {
+        const u32x4 v{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                      __float_as_uint(f[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, aux);
+    } else if constexpr (sizeof(T) == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f[0]), r, (int)off, 0, aux);
+    } else if constexpr (VEC == 8 && kSplitCvt) {
+        const u32x4 v{pack_bf16x2_split(f[0], f[1]), pack_bf16x2_split(f[2], f[3]),
+                      pack_bf16x2_split(f[4], f[5]), pack_bf16x2_split(f[6], f[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, aux);
+    } else if constexpr (VEC == 8) {
+        const u32x4 v{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                      pack_bf16x2(f[6], f[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, aux);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)f[0]), r,
+                                              (int)off, 0, aux);
+    }
+}
+
 // Products for the per-row fp64 sums.  For bf16 inputs the fp32 products are
 // exact (8-bit significands: a square has 16 bits, w*dy*x has 24), so the
 // fp32 multiply loses nothing; for fp32 inputs they are formed in fp64.

@@ -116,46 +116,47 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
         }
     };
 
-    // One row block's operands.  Loads are issued without branches: lanes
-    // outside the tensor (rows past the end, columns past H) read the first
-    // bytes of this workgroup's own partial row instead (one line per
-    // wavefront; the partial row is written only by this workgroup, at the
-    // end) and are masked where the values are used.  With the same number
-    // of loads on every path the compiler waits for exactly the block it is
-    // about to use while the next block's loads stay in flight.
+    // One row block's operands, read through buffer resources sized to the
+    // rows of the block that exist: lanes of rows past the end, and lanes of
+    // columns past H (offset kBufOutside), load zeros and their stores are
+    // dropped.  Every lane issues the same loads on every path, so the
+    // compiler waits for exactly the block it is about to use while the
+    // next block's loads stay in flight.
     struct Blk {
         Pack<T, VEC> x[NCH], dy[NCH], dr[DRES ? NCH : 1];
         float rs;
     };
-    const float* dummyf = partial + (int64_t)blockIdx.x * ldp;
-    const T* dummy = reinterpret_cast<const T*>(dummyf);
+    uint32_t voff[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = (c * TEAM + lt) * VEC;
+        voff[c] = col < H ? (uint32_t)(team * H + col) * (uint32_t)sizeof(T) : kBufOutside;
+    }
+    auto block_rows = [&](int64_t b) -> uint32_t {  // rows of block b that exist (b < end)
+        return (uint32_t)(end - b < R ? end - b : R);
+    };
     auto issue = [&](int64_t b, Blk& q) {
-        const int64_t row = b + team;
-        const bool active = row < end;
-        const int64_t off = row * (int64_t)H;
+        const int64_t off = b * (int64_t)H;
+        const uint32_t nr = block_rows(b);
+        const uint32_t bytes = nr * (uint32_t)H * (uint32_t)sizeof(T);
+        const BufRes rx = buf_rsrc(x + off, bytes);
+        const BufRes rdy = buf_rsrc(dy + off, bytes);
+        const BufRes rdr = buf_rsrc(DRES ? dres + off : x, DRES ? bytes : 0u);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int col = (c * TEAM + lt) * VEC;
-            const bool ok = active && col < H;
-            q.x[c] = load_pack<T, VEC, kNtLoad>(ok ? x + off + col : dummy);
-            q.dy[c] = load_pack<T, VEC, kNtLoad>(ok ? dy + off + col : dummy);
-            if constexpr (DRES) q.dr[c] = load_pack<T, VEC, kNtLoad>(ok ? dres + off + col : dummy);
+            q.x[c] = buf_load_pack<T, VEC, kNtLoad>(rx, voff[c]);
+            q.dy[c] = buf_load_pack<T, VEC, kNtLoad>(rdy, voff[c]);
+            if constexpr (DRES) q.dr[c] = buf_load_pack<T, VEC, kNtLoad>(rdr, voff[c]);
         }
-        q.rs = *((has_rstd && active) ? rstd + row : dummyf);
+        // Without a saved statistic the resource is empty (size 0), so the
+        // load returns zero and reads nothing.
+        const BufRes rr = has_rstd ? buf_rsrc(rstd + b, nr * 4u) : buf_rsrc(x, 0u);
+        q.rs = buf_load_f32(rr, (uint32_t)team * 4u);
     };
 
     auto process = [&](int64_t b, Blk& q, int set) {
         const int64_t row = b + team;
         const bool active = row < end;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int col = (c * TEAM + lt) * VEC;
-            if (!(active && col < H)) {
-                q.x[c] = zero_pack<T, VEC>();
-                q.dy[c] = zero_pack<T, VEC>();
-                if constexpr (DRES) q.dr[c] = zero_pack<T, VEC>();
-            }
-        }
         // Pass A: row sums.  Values are unpacked again in pass B rather than
         // kept live across the reduction (unpacking is a shift or a mask).
         double cs = 0.0, ss = 0.0;
@@ -188,8 +189,10 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
         const double kk = r * r * (cs * inv_h);
         const float k_hi = (float)kk;
         const float k_lo = (float)(kk - (double)k_hi);
-        // Pass B: dx and the dw column sums (masked lanes hold zeros, so
-        // they add nothing to the sums).
+        // Pass B: dx and the dw column sums (lanes outside the tensor hold
+        // zeros, so they add nothing to the sums).
+        const BufRes rdx = buf_rsrc(dx + b * (int64_t)H,
+                                    block_rows(b) * (uint32_t)H * (uint32_t)sizeof(T));
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             float xv[VEC], dyv[VEC], wc[VEC], o[VEC];
@@ -223,8 +226,7 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
                     acc[c][k] += (dyv[k] * xv[k]) * rf;
                 }
             }
-            const int col = (c * TEAM + lt) * VEC;
-            if (active && col < H) store_vec<T, VEC, kNtStore, DRES>(dx + row * (int64_t)H + col, o);
+            buf_store_vec<T, VEC, kNtStore, DRES>(rdx, voff[c], o);
         }
     };
 
@@ -417,21 +419,19 @@ int partial_ld(int64_t H) { return (int)((H + 63) / 64 * 64); }
 
 template <typename T, int VEC, int TEAM, int NCH>
 static hipError_t launch_rows_cfg(const BwdArgs& a, hipStream_t s) {
-    // Workgroup size by bytes per lane (EB): small tiles share 1024-lane
-    // workgroups among several rows, larger tiles use smaller workgroups so
-    // that the row, its prefetched successor, w and the dw sums stay in
-    // registers.  Teams wider than that fill the workgroup alone.
-    // A one-chunk team of 512 lanes or more is a workgroup of its own.
+    // Workgroup size by bytes per lane (EB): 512 lanes, shared among several
+    // rows by narrow tiles, and 256 for tiles of more than 32 bytes per lane
+    // so that the row, its prefetched successor, w and the dw sums stay in
+    // registers.  Teams wider than that fill the workgroup alone, and a
+    // one-chunk team of 512 lanes or more is a workgroup of its own.
+    // 1024-lane groups for the narrow tiles measured slower (bf16 262144 x
+    // 128 row pass 36.0 -> 34.5 us with 512 lanes; with a residual-stream
+    // gradient, whose 1024-lane form spilled in the row loop, 51.2 -> 47.9).
     constexpr int EB = NCH * VEC * (int)sizeof(T);
-    constexpr int WGD = (TEAM >= 512 && NCH == 1) ? TEAM : (EB <= 16 ? 1024 : (EB <= 32 ? 512 : 256));
+    constexpr int WGD = (TEAM >= 512 && NCH == 1) ? TEAM : (EB <= 32 ? 512 : 256);
     constexpr int WG = TEAM > WGD ? TEAM : WGD;
-    // With a residual-stream gradient each block holds one more row tensor;
-    // in 1024-lane groups (128 VGPRs) that spills inside the row loop, so the
-    // residual kind of those tiles runs 512-lane groups (measured on bf16
-    // 262144 x 128: 51.2 -> 47.9 us; the other tiles are unchanged).
-    constexpr int WGR = (WG == 1024 && TEAM < 1024) ? 512 : WG;
     if (a.dres) {
-        hipLaunchKernelGGL((bwd_rows_kernel<T, VEC, TEAM, NCH, WGR, true>), dim3(a.G), dim3(WGR), 0,
+        hipLaunchKernelGGL((bwd_rows_kernel<T, VEC, TEAM, NCH, WG, true>), dim3(a.G), dim3(WG), 0,
                            s, (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
                            (const T*)a.dres, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
     } else {

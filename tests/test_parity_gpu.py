@@ -365,13 +365,20 @@ def test_rows_zero():
     assert (dw == 0).all()
 
 
-def test_guard_bands_untouched():
+# A partly filled last row block on every tile kind (rows per block 64, 8, 2,
+# 1, 4) and the scalar path.
+GUARD = [(synth.BF16, 129, 896), (synth.BF16, 300, 128), (synth.BF16, 3, 4096),
+         (synth.BF16, 1539, 4096), (synth.BF16, 5, 8192), (synth.BF16, 7, 500),
+         (synth.F32, 2053, 896), (synth.F32, 5, 4095)]
+
+
+@pytest.mark.parametrize("dtype,rows,H", GUARD)
+def test_guard_bands_untouched(dtype, rows, H):
     """Outputs sit between sentinel bands; the kernels write every output
     element and nothing outside."""
-    rows, H, dtype = 129, 896, synth.BF16
     wl, x, w, dy, res, dres = _inputs(rows, H, dtype, seed=3)
     G = 4096
-    td = torch.bfloat16
+    td = torch_dtype(dtype)
 
     def banded(n):
         buf = torch.full((n + 2 * G,), 12345.0, dtype=td, device=DEV)
@@ -385,15 +392,24 @@ def test_guard_bands_untouched():
     dwb, dw = banded(H)
     rb = torch.full((rows + 2 * G,), 777.0, device=DEV)
     rstd = rb[G:G + rows]
+    y2b, y2 = banded(rows * H)
+    dx2b, dx2 = banded(rows * H)
+    dw2b, dw2 = banded(H)
+    rb2 = torch.full((rows + 2 * G,), 777.0, device=DEV)
+    rstd2 = rb2[G:G + rows]
     B.rmsnorm_residual_fwd(xd, rd, wd, h.view(rows, H), y.view(rows, H), rstd, wl.eps)
     B.rmsnorm_bwd(dyd, h.view(rows, H), wd, rstd, drd, dx.view(rows, H), dw, _ws(rows, H, dtype),
                   wl.eps)
+    B.rmsnorm_fwd(xd, wd, y2.view(rows, H), rstd2, wl.eps)
+    B.rmsnorm_bwd(dyd, xd, wd, rstd2, None, dx2.view(rows, H), dw2, _ws(rows, H, dtype), wl.eps)
     torch.cuda.synchronize()
-    for buf, n in ((hb, rows * H), (yb, rows * H), (dxb, rows * H), (dwb, H)):
+    for buf, n in ((hb, rows * H), (yb, rows * H), (dxb, rows * H), (dwb, H),
+                   (y2b, rows * H), (dx2b, rows * H), (dw2b, H)):
         assert (buf[:G] == 12345.0).all() and (buf[G + n:] == 12345.0).all()
         assert not torch.isnan(buf[G:G + n]).any()
-    assert (rb[:G] == 777.0).all() and (rb[G + rows:] == 777.0).all()
-    assert not torch.isnan(rstd).any()
+    for band, r in ((rb, rstd), (rb2, rstd2)):
+        assert (band[:G] == 777.0).all() and (band[G + rows:] == 777.0).all()
+        assert not torch.isnan(r).any()
 
 
 @pytest.mark.parametrize("dtype,rows,H,mode", [
