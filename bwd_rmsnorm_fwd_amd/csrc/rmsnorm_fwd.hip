@@ -12,19 +12,19 @@
 // from HBM exactly once.  Loads/stores are 128-bit per lane and contiguous
 // across the team.  The sum of squares is exact-product fp32 accumulated in
 // fp64 per lane, reduced with DPP inside 16-lane rows and lane reads across
-// rows (LDS across wavefronts).  The grid gives every workgroup at least
-// RMS_FWD_WG_BYTES of x (one row block for rows of 8 KB and more, a few
-// blocks for narrow rows); workgroups that get more than one block prefetch
-// the next while finishing the current one.
+// rows (LDS across wavefronts).  The grid has one workgroup per row block up
+// to RMS_FWD_MAX_GRID workgroups; beyond that a workgroup takes several
+// blocks and prefetches the next while finishing the current one.
 #include "common.hpp"
 #include "launch.hpp"
 
 // Grid size: ceil(bytes of x / RMS_FWD_WG_BYTES), at least RMS_FWD_MIN_GRID
-// and at most one workgroup per row block (measured: one block per workgroup
-// is best for rows of 8 KB and more, e.g. 87 vs 92 us for the bf16 residual
-// forward at 16384 x 4096; two 4 KB blocks per workgroup for 128-wide rows).
+// and at most one workgroup per row block.  Measured: one block per
+// workgroup is best at every width (bf16 residual 16384 x 4096: 87 vs 92 us
+// against a fixed 4096-workgroup grid; bf16 262144 x 128, 4 KB blocks: 23.2
+// -> 23.0 us for one block per workgroup instead of two).
 #ifndef RMS_FWD_WG_BYTES
-#define RMS_FWD_WG_BYTES 8192
+#define RMS_FWD_WG_BYTES 4096
 #endif
 #ifndef RMS_FWD_MIN_GRID
 #define RMS_FWD_MIN_GRID 2048
@@ -87,20 +87,31 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
         }
     }
 
+    // Row blocks are read and written through buffer resources sized to the
+    // block's rows that exist; lanes of rows past the end, and of columns
+    // past H (offset kBufOutside), load zeros and their stores are dropped.
     struct RowRegs {
         Pack<T, VEC> x[NCH], r[RES ? NCH : 1];
     };
+    uint32_t voff[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = (c * TEAM + lt) * VEC;
+        voff[c] = col < H ? (uint32_t)(team * H + col) * (uint32_t)sizeof(T) : kBufOutside;
+    }
+    auto block_bytes = [&](int64_t rb) -> uint32_t {  // bytes of block rb's rows (rb < nrb)
+        const int64_t left = rows - rb * R;
+        return (uint32_t)(left < R ? left : R) * (uint32_t)H * (uint32_t)sizeof(T);
+    };
     auto load_row = [&](int64_t rb, RowRegs& q) {
-        const int64_t row = rb * R + team;
-        const bool active = row < rows;
-        const int64_t off = row * (int64_t)H;
+        const int64_t off = rb * R * (int64_t)H;
+        const uint32_t bytes = block_bytes(rb);
+        const BufRes rx = buf_rsrc(x + off, bytes);
+        const BufRes rr = buf_rsrc(RES ? res + off : x, RES ? bytes : 0u);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int col = (c * TEAM + lt) * VEC;
-            const bool ok = active && col < H;
-            q.x[c] = ok ? load_pack<T, VEC, kNtLoad>(x + off + col) : zero_pack<T, VEC>();
-            if constexpr (RES)
-                q.r[c] = ok ? load_pack<T, VEC, kNtLoad>(res + off + col) : zero_pack<T, VEC>();
+            q.x[c] = buf_load_pack<T, VEC, kNtLoad>(rx, voff[c]);
+            if constexpr (RES) q.r[c] = buf_load_pack<T, VEC, kNtLoad>(rr, voff[c]);
         }
     };
 
@@ -128,7 +139,10 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
 
         const int64_t row = rb * R + team;
         const bool active = row < rows;
-        const int64_t off = row * (int64_t)H;
+        const int64_t boff = rb * R * (int64_t)H;
+        const uint32_t bbytes = block_bytes(rb);
+        const BufRes ry = buf_rsrc(y + boff, bbytes);
+        const BufRes rh = buf_rsrc(RES ? h + boff : y, RES ? bbytes : 0u);
         float v[NCH][VEC];
         double ss = 0.0;
 #pragma unroll
@@ -139,8 +153,7 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
                 unpack(cur.r[c], rv);
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) v[c][k] = round_to(v[c][k] + rv[k], (T*)nullptr);
-                const int col = (c * TEAM + lt) * VEC;
-                if (active && col < H) store_vec<T, VEC, kNtStore>(h + off + col, v[c]);
+                buf_store_vec<T, VEC, kNtStore>(rh, voff[c], v[c]);
             }
 #pragma unroll
             for (int k = 0; k < VEC; ++k) ss += sq64(v[c][k], (T*)nullptr);
@@ -161,7 +174,7 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
             }
 #pragma unroll
             for (int k = 0; k < VEC; ++k) o[k] = (v[c][k] * rf) * wc[k];
-            if (active && col < H) store_vec<T, VEC, kNtStore>(y + off + col, o);
+            buf_store_vec<T, VEC, kNtStore>(ry, voff[c], o);
         }
 
         if constexpr (kDepth > 0) {
