@@ -30,22 +30,10 @@ __device__ __forceinline__ u32x4 ld128(const void* p) {
     else return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Streaming stores are nontemporal with device scope (nt sc1), so the line is
-// written through the XCD's L2 rather than left dirty there for the write-back
-// at the end of the kernel (measured on the bf16 4096 x 4096 forward +
-// backward step: 35.2-35.5 -> 34.9-35.0 us, backward row pass 19.6 -> 19.4
-// us).  No builtin sets these bits on a global store, so it is written as
-// inline assembly; the s_nop gives the wait state that a following write of
-// the data registers needs after a store wider than 8 bytes, which the
-// compiler cannot insert for an instruction inside inline assembly.
 template <bool NT>
 __device__ __forceinline__ void st128(void* p, u32x4 v) {
-    if constexpr (NT) {
-        asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 0" ::"v"(p), "v"(v)
-                     : "memory");
-    } else {
-        *reinterpret_cast<u32x4*>(p) = v;
-    }
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -129,7 +117,7 @@ __device__ __forceinline__ void unpack(const Pack<T, VEC>& p, float (&f)[VEC]) {
     }
 }
 
-template <typename T, int VEC, bool NT = false, bool kSplitCvt = false>
+template <typename T, int VEC, bool NT = false>
 __device__ __forceinline__ void store_vec(T* p, const float (&f)[VEC]) {
     if constexpr (sizeof(T) == 4 && VEC == 4) {
         st128<NT>(p, u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
@@ -137,9 +125,6 @@ __device__ __forceinline__ void store_vec(T* p, const float (&f)[VEC]) {
     } else if constexpr (sizeof(T) == 4 && VEC == 1) {
         if constexpr (NT) __builtin_nontemporal_store(f[0], reinterpret_cast<float*>(p));
         else *reinterpret_cast<float*>(p) = f[0];
-    } else if constexpr (VEC == 8 && kSplitCvt) {
-        st128<NT>(p, u32x4{pack_bf16x2_split(f[0], f[1]), pack_bf16x2_split(f[2], f[3]),
-                           pack_bf16x2_split(f[4], f[5]), pack_bf16x2_split(f[6], f[7])});
     } else if constexpr (VEC == 8) {
         st128<NT>(p, u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
                        pack_bf16x2(f[6], f[7])});
@@ -188,8 +173,11 @@ __device__ __forceinline__ float buf_load_f32(BufRes r, uint32_t off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
 
-// store_vec through a resource; streaming (NT) stores are nontemporal with
-// device scope, as st128's.
+// store_vec through a resource.  Streaming (NT) stores are nontemporal with
+// device scope (nt sc1), so the line is written through the XCD's L2 rather
+// than left dirty there for the write-back at the end of the kernel
+// (measured on the bf16 4096 x 4096 forward + backward step: 35.2-35.5 ->
+// 34.9-35.0 us against nontemporal stores alone).
 template <typename T, int VEC, bool NT = false, bool kSplitCvt = false>
 __device__ __forceinline__ void buf_store_vec(BufRes r, uint32_t off, const float (&f)[VEC]) {
     constexpr int aux = NT ? (kAuxNt | kAuxSc1) : 0;

@@ -47,10 +47,6 @@
 #ifndef RMS_BWD_PREFETCH
 #define RMS_BWD_PREFETCH 1
 #endif
-// Nontemporal stores for the dw partial rows (read once, by the reduce pass).
-#ifndef RMS_BWD_PART_NT
-#define RMS_BWD_PART_NT 0
-#endif
 
 namespace rms {
 
@@ -270,12 +266,11 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     // With VEC > 1, H is a multiple of VEC, so groups of four columns that
     // start below H end below H (and below HT); ldp is a multiple of 64.
     float* prow = partial + (int64_t)blockIdx.x * ldp;
-    constexpr bool kPartNt = RMS_BWD_PART_NT != 0;
     auto store4 = [&](int col, float a, float b, float c, float d) {
         u32x4 v;
         v.x = __float_as_uint(a); v.y = __float_as_uint(b);
         v.z = __float_as_uint(c); v.w = __float_as_uint(d);
-        st128<kPartNt>(prow + col, v);
+        st128<false>(prow + col, v);
     };
     if constexpr (R == 1) {
 #pragma unroll
