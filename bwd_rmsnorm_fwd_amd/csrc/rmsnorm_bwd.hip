@@ -50,6 +50,59 @@
 
 namespace rms {
 
+// Per-row factors of dx (P1 §5.3): r, k = r^2 c, and k split into two floats
+// for the fp32 form.  rf is the dw scale: zero for rows past the end, so
+// neither the r of their zero inputs (infinite at eps = 0) nor whatever
+// their rstd lane read can turn the 0 * r products into NaN.
+struct RowK {
+    double r, kk;
+    float rf, k_hi, k_lo;
+};
+
+__device__ __forceinline__ RowK row_k(double r, double cs, double inv_h, bool active) {
+    RowK q;
+    q.r = r;
+    q.rf = active ? (float)r : 0.f;
+    q.kk = r * r * (cs * inv_h);
+    q.k_hi = (float)q.kk;
+    q.k_lo = (float)(q.kk - (double)q.k_hi);
+    return q;
+}
+
+// dx of one chunk, dx = r (w dy - x k) [+ dres] (P1 §5.3), and its dw terms
+// dy x r added to acc (P1 §5.4; lanes outside the tensor hold zeros and add
+// nothing).
+template <typename T, int VEC, bool DRES>
+__device__ __forceinline__ void dx_chunk(const float (&xv)[VEC], const float (&dyv)[VEC],
+                                         const float (&wc)[VEC], const float (&drv)[VEC],
+                                         const RowK& q, float (&o)[VEC], float (&acc)[VEC]) {
+    if constexpr (DRES || sizeof(T) == 4) {
+        // fp64 form: w*dy (exact in fp64), r*(wdy - x k) [+ dres] with one
+        // final rounding.  Used when dx can cancel against dres, and for fp32
+        // inputs, whose w*dy is not exact in fp32.
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const double wdy = (double)wc[k] * (double)dyv[k];
+            const double t = __builtin_fma(-(double)xv[k], q.kk, wdy);
+            if constexpr (DRES) o[k] = (float)__builtin_fma(q.r, t, (double)drv[k]);
+            else o[k] = (float)(q.r * t);
+            acc[k] += (dyv[k] * xv[k]) * q.rf;
+        }
+    } else {
+        // bf16 inputs: w*dy is exact in fp32, and two fused multiply-adds
+        // with k = k_hi + k_lo form wdy - x k to fp32 accuracy even where the
+        // two terms nearly cancel.
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const float wdy = wc[k] * dyv[k];
+            float t = __builtin_fmaf(-xv[k], q.k_hi, wdy);
+            t = __builtin_fmaf(-xv[k], q.k_lo, t);
+            o[k] = q.rf * t;
+            acc[k] += (dyv[k] * xv[k]) * q.rf;
+        }
+    }
+}
+
 template <typename T, int VEC, int TEAM, int NCH, int WG, bool DRES>
 __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __restrict__ x,
                                                       const T* __restrict__ w,
@@ -177,51 +230,18 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
             ss = team_sum_alt<TEAM>(ss, rs_slots + R * NWT);
             r = rsqrt_f64(ss * inv_h + (double)eps);
         }
-        // Rows past the end add nothing to dw: their scale is zero, not the
-        // r of zero inputs (infinite at eps = 0) or the value their rstd
-        // lane read from the workspace (whatever the caller's buffer held),
-        // either of which would turn the 0 * r products into NaN.
-        const float rf = active ? (float)r : 0.f;
-        const double kk = r * r * (cs * inv_h);
-        const float k_hi = (float)kk;
-        const float k_lo = (float)(kk - (double)k_hi);
-        // Pass B: dx and the dw column sums (lanes outside the tensor hold
-        // zeros, so they add nothing to the sums).
+        const RowK kq = row_k(r, cs, inv_h, active);
+        // Pass B: dx and the dw column sums.
         const BufRes rdx = buf_rsrc(dx + b * (int64_t)H,
                                     block_rows(b) * (uint32_t)H * (uint32_t)sizeof(T));
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            float xv[VEC], dyv[VEC], wc[VEC], o[VEC];
+            float xv[VEC], dyv[VEC], wc[VEC], drv[VEC], o[VEC];
             unpack(q.x[c], xv);
             unpack(q.dy[c], dyv);
             weights(c, wc);
-            if constexpr (DRES || sizeof(T) == 4) {
-                // fp64 form: w*dy (exact in fp64), r*(wdy - x k) [+ dres] with
-                // one final rounding.  Used when dx can cancel against dres,
-                // and for fp32 inputs, whose w*dy is not exact in fp32.
-                float drv[VEC];
-                if constexpr (DRES) unpack(q.dr[c], drv);
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    const double wdy = (double)wc[k] * (double)dyv[k];
-                    const double t = __builtin_fma(-(double)xv[k], kk, wdy);
-                    if constexpr (DRES) o[k] = (float)__builtin_fma(r, t, (double)drv[k]);
-                    else o[k] = (float)(r * t);
-                    acc[c][k] += (dyv[k] * xv[k]) * rf;
-                }
-            } else {
-                // bf16 inputs: w*dy is exact in fp32, and two fused multiply-
-                // adds with k = k_hi + k_lo form wdy - x k to fp32 accuracy
-                // even where the two terms nearly cancel.
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    const float wdy = wc[k] * dyv[k];
-                    float t = __builtin_fmaf(-xv[k], k_hi, wdy);
-                    t = __builtin_fmaf(-xv[k], k_lo, t);
-                    o[k] = rf * t;
-                    acc[c][k] += (dyv[k] * xv[k]) * rf;
-                }
-            }
+            if constexpr (DRES) unpack(q.dr[c], drv);
+            dx_chunk<T, VEC, DRES>(xv, dyv, wc, drv, kq, o, acc[c]);
             buf_store_vec<T, VEC, kNtStore, DRES>(rdx, voff[c], o);
         }
     };
@@ -334,6 +354,152 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     }
 }
 
+// Rows too wide for the register tiles (1024-lane teams with 4 or more
+// chunks per lane).  Holding such a row in registers across its row sum
+// spills, so a workgroup of WW lanes owns one row at a time and streams it
+// twice in slices of WW * VEC elements: pass A forms the row sums, pass B reads
+// each slice again (from L2 or the Infinity Cache: pass A's loads are
+// cached, pass B's are the last use) to form dx and the dw terms.  Only the
+// dw column sums stay in registers (NS x VEC per lane).  The next slice's
+// loads are in flight while the current one is used, also across the pass
+// and row boundaries.  Rows are dealt round-robin to the G workgroups; each
+// writes one partial row of dw sums, as bwd_rows_kernel does.  Workgroups
+// of WW = 1024 lanes up to 4 slices; wider rows use 512 lanes, whose waves
+// have twice the registers for the larger share of dw sums.
+constexpr int kWideTeam = 1024;  // the geometry table's team for these rows
+
+template <typename T, int VEC, int WW, int NS, bool DRES>
+__global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
+    const T* dy, const T* __restrict__ x, const T* __restrict__ w,
+    const float* __restrict__ rstd, const T* dres, T* dx, float* __restrict__ partial,
+    int64_t rows, int H, int ldp, float eps) {
+    static_assert(NS >= 2 && (NS & (NS - 1)) == 0, "NS: a power of two, at least 2");
+    constexpr int NWT = WW / kWave;
+    constexpr int SL = WW * VEC;  // elements per slice
+    constexpr bool kNtLoad = DRES ? RMS_DRES_NT_LOAD != 0 : RMS_BWD_NT_LOAD != 0;
+    constexpr bool kNtStore = DRES ? RMS_DRES_NT_STORE != 0 : RMS_BWD_NT_STORE != 0;
+    // Two slot sets used by alternate rows, each for c and sum x^2.
+    __shared__ double red[2 * 2 * NWT];
+
+    const int lt = threadIdx.x;
+    const bool has_rstd = rstd != nullptr;
+    const double inv_h = 1.0 / (double)H;
+    const uint32_t row_bytes = (uint32_t)H * (uint32_t)sizeof(T);
+    // The lane's offset in slice s; chunks past H (and slices past the row)
+    // read zeros and are not stored.  Formed when used rather than kept: the
+    // registers go to the dw sums.
+    const int lcol = lt * VEC;
+    auto voff = [&](int s) -> uint32_t {
+        const int col = s * SL + lcol;
+        return col < H ? (uint32_t)col * (uint32_t)sizeof(T) : kBufOutside;
+    };
+    const BufRes rw = buf_rsrc(w, row_bytes);
+    float acc[NS][VEC];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[s][k] = 0.f;
+    }
+
+    struct Slice {
+        Pack<T, VEC> x, dy, w, dr;
+    };
+    // Pass A's loads: row `row` if it exists (else an empty resource: the
+    // loads return zeros and read nothing), cached for pass B.
+    auto load_a = [&](int64_t row, int s, Slice& q) {
+        const bool ok = row < rows;
+        const int64_t off = ok ? row * (int64_t)H : 0;
+        const uint32_t n = ok ? row_bytes : 0u;
+        q.x = buf_load_pack<T, VEC>(buf_rsrc(x + off, n), voff(s));
+        q.dy = buf_load_pack<T, VEC>(buf_rsrc(dy + off, n), voff(s));
+        q.w = buf_load_pack<T, VEC>(rw, voff(s));
+    };
+    auto load_b = [&](int64_t row, int s, Slice& q) {
+        const int64_t off = row * (int64_t)H;
+        q.x = buf_load_pack<T, VEC, kNtLoad>(buf_rsrc(x + off, row_bytes), voff(s));
+        q.dy = buf_load_pack<T, VEC, kNtLoad>(buf_rsrc(dy + off, row_bytes), voff(s));
+        q.w = buf_load_pack<T, VEC>(rw, voff(s));
+        if constexpr (DRES) q.dr = buf_load_pack<T, VEC, kNtLoad>(buf_rsrc(dres + off, row_bytes), voff(s));
+    };
+
+    const int64_t G = gridDim.x;
+    Slice buf[2];
+    int set = 0;
+    int64_t row = blockIdx.x;
+    load_a(row, 0, buf[0]);
+    for (; row < rows; row += G, set ^= 1) {
+        // Pass A: the row sums, slice s while slice s + 1 loads (after the
+        // last slice, pass B's first).
+        double cs = 0.0, ss = 0.0;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if (s + 1 < NS) load_a(row, s + 1, buf[(s + 1) & 1]);
+            else load_b(row, 0, buf[0]);
+            const Slice& q = buf[s & 1];
+            float xv[VEC], dyv[VEC], wc[VEC];
+            unpack(q.x, xv);
+            unpack(q.dy, dyv);
+            unpack(q.w, wc);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                cs += prod3_64(wc[k], dyv[k], xv[k], (T*)nullptr);
+                if (!has_rstd) ss += sq64(xv[k], (T*)nullptr);
+            }
+            // Keep the schedule one slice ahead: without this fence the
+            // unrolled slices' loads are hoisted together and spill.
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        double* slots = red + set * 2 * NWT;
+        cs = team_sum_alt<WW>(cs, slots);
+        double r;
+        if (has_rstd) {
+            r = (double)rstd[row];
+        } else {
+            ss = team_sum_alt<WW>(ss, slots + NWT);
+            r = rsqrt_f64(ss * inv_h + (double)eps);
+        }
+        const RowK kq = row_k(r, cs, inv_h, true);
+        // Pass B: dx and the dw terms, slice s while slice s + 1 loads
+        // (after the last slice, the next row's first).
+        const BufRes rdx = buf_rsrc(dx + row * (int64_t)H, row_bytes);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if (s + 1 < NS) load_b(row, s + 1, buf[(s + 1) & 1]);
+            else load_a(row + G, 0, buf[0]);
+            const Slice& q = buf[s & 1];
+            float xv[VEC], dyv[VEC], wc[VEC], drv[VEC], o[VEC];
+            unpack(q.x, xv);
+            unpack(q.dy, dyv);
+            unpack(q.w, wc);
+            if constexpr (DRES) unpack(q.dr, drv);
+            dx_chunk<T, VEC, DRES>(xv, dyv, wc, drv, kq, o, acc[s]);
+            buf_store_vec<T, VEC, kNtStore, DRES>(rdx, voff(s), o);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // The workgroup's partial row (zeros if it had no rows).
+    float* prow = partial + (int64_t)blockIdx.x * ldp;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int col = s * SL + lt * VEC;
+        if (col < H) {
+            if constexpr (VEC == 1) {
+                prow[col] = acc[s][0];
+            } else {
+#pragma unroll
+                for (int k = 0; k < VEC; k += 4) {
+                    u32x4 v;
+                    v.x = __float_as_uint(acc[s][k]);
+                    v.y = __float_as_uint(acc[s][k + 1]);
+                    v.z = __float_as_uint(acc[s][k + 2]);
+                    v.w = __float_as_uint(acc[s][k + 3]);
+                    st128<false>(prow + col + k, v);
+                }
+            }
+        }
+    }
+}
+
 // dw[j] = sum_{g < G} partial[g][j] in a fixed order.  A workgroup of
 // kRedWG lanes owns kRedCols columns (kRedCL lanes x 4 columns, 128-bit
 // loads) and kRedGL lanes over g: lane gl adds rows g = gl, gl + kRedGL, ...
@@ -437,16 +603,47 @@ static hipError_t launch_rows_cfg(const BwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Rows the geometry table gives a 1024-lane team with 4 or more chunks per
+// lane (wider than 16384 bf16 or 8192 fp32 elements with 128-bit access,
+// 2048 with scalar access): the streaming kernel, in 1024-lane workgroups
+// when the row takes at most 4 slices of them, else in 512-lane workgroups,
+// with the smallest power-of-two slice count that covers the row.  Measured against the register tiles: bf16 2048 x 32768 row pass 135.6
+// -> 97.5 us, 1024 x 65536 340.5 -> 129.6, 2048 x 32768 with dres 242.5 ->
+// 115.1; at 4096 x 16384 the 1024 x 2 tile stays (84.5 vs 94.0).
+template <typename T, int VEC, int WW, int NS>
+static hipError_t launch_wide_cfg(const BwdArgs& a, hipStream_t s) {
+    if (a.dres) {
+        hipLaunchKernelGGL((bwd_rows_wide_kernel<T, VEC, WW, NS, true>), dim3(a.G), dim3(WW), 0, s,
+                           (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
+                           (const T*)a.dres, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
+    } else {
+        hipLaunchKernelGGL((bwd_rows_wide_kernel<T, VEC, WW, NS, false>), dim3(a.G), dim3(WW), 0, s,
+                           (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
+                           (const T*)nullptr, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int VEC>
+static hipError_t launch_rows_wide(const BwdArgs& a, hipStream_t s) {
+    const int64_t n1024 = (a.H + 1024 * VEC - 1) / (1024 * VEC);
+    if (n1024 <= 4) return launch_wide_cfg<T, VEC, 1024, 4>(a, s);
+    const int64_t n512 = (a.H + 512 * VEC - 1) / (512 * VEC);
+    if (n512 <= 16) return launch_wide_cfg<T, VEC, 512, 16>(a, s);
+    if (n512 <= 32) return launch_wide_cfg<T, VEC, 512, 32>(a, s);
+    return hipErrorInvalidValue;
+}
+
 template <typename T, int VEC>
 static hipError_t dispatch_rows(const BwdArgs& a, hipStream_t s) {
     Geometry g;
     if (!choose_geometry(a.H, VEC, a.dres != nullptr, &g)) return hipErrorInvalidValue;
+    if (g.team == kWideTeam && g.nch >= 4) return launch_rows_wide<T, VEC>(a, s);
 #define RMS_CASE(TM, NC) \
     if (g.team == TM && g.nch == NC) return launch_rows_cfg<T, VEC, TM, NC>(a, s);
     RMS_CASE(1, 1) RMS_CASE(2, 1) RMS_CASE(4, 1) RMS_CASE(8, 1) RMS_CASE(16, 1) RMS_CASE(32, 1)
     RMS_CASE(64, 1) RMS_CASE(64, 2) RMS_CASE(128, 2) RMS_CASE(256, 2) RMS_CASE(512, 1)
-    RMS_CASE(512, 2)
-    RMS_CASE(1024, 2) RMS_CASE(1024, 4) RMS_CASE(1024, 8) RMS_CASE(1024, 16)
+    RMS_CASE(512, 2) RMS_CASE(1024, 2)
 #undef RMS_CASE
     return hipErrorInvalidValue;
 }

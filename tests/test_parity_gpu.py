@@ -139,7 +139,7 @@ def test_bwd_multi_block(dtype, rows, H, mode):
 # shape leaves at least one workgroup with a partly filled last block.
 STALE = [(synth.BF16, 300, 128), (synth.BF16, 3, 4096), (synth.BF16, 1539, 4096),
          (synth.BF16, 33, 896), (synth.F32, 2053, 896), (synth.BF16, 7, 500),
-         (synth.F32, 5, 4095), (synth.BF16, 775, 8192)]
+         (synth.F32, 5, 4095), (synth.BF16, 775, 8192), (synth.BF16, 19, 32768)]
 
 
 @pytest.mark.parametrize("fill", ["nan", "inf", "-inf"])
@@ -369,7 +369,8 @@ def test_rows_zero():
 # 1, 4) and the scalar path.
 GUARD = [(synth.BF16, 129, 896), (synth.BF16, 300, 128), (synth.BF16, 3, 4096),
          (synth.BF16, 1539, 4096), (synth.BF16, 5, 8192), (synth.BF16, 7, 500),
-         (synth.F32, 2053, 896), (synth.F32, 5, 4095)]
+         (synth.F32, 2053, 896), (synth.F32, 5, 4095), (synth.BF16, 9, 32768),
+         (synth.F32, 5, 12289)]
 
 
 @pytest.mark.parametrize("dtype,rows,H", GUARD)
@@ -518,8 +519,7 @@ def test_graph_capture_replays_match_eager(rows, H):
                                           (synth.BF16, 2, 30000), (synth.F32, 2, 16384),
                                           (synth.F32, 1, 65536)])
 def test_widest_rows(dtype, rows, H):
-    """The 1024-lane tiles with 4-16 chunks per lane (their backward spills
-    registers: slower, still exact to the same bars) and H = RMSNORM_MAX_H."""
+    """The widest rows, up to H = RMSNORM_MAX_H, through the residual pair."""
     wl, x, w, dy, res, dres = _inputs(rows, H, dtype, seed=H + rows)
     xd, wd, dyd, rd, drd = (to_dev(a, dtype) for a in (x, w, dy, res, dres))
     h, y, dx = _empty(rows, H, dtype), _empty(rows, H, dtype), _empty(rows, H, dtype)
@@ -536,6 +536,39 @@ def test_widest_rows(dtype, rows, H):
     assert_rstd(f64(rstd), ro)
     dxo, dwo = oracle.rmsnorm_bwd(synth.to_f64(dy, dtype), ho, synth.to_f64(w, dtype), wl.eps,
                                   rstd=f64(rstd), dres=synth.to_f64(dres, dtype))
+    assert_output("dx", f64(dx), dxo, dtype)
+    assert_dw(f64(dw), dwo, dtype)
+
+
+# Rows served by the streaming backward (the geometry's 1024-lane teams with
+# 4 or more chunks per lane: 1024-lane workgroups with 4 slices, 512-lane
+# ones with 16 and 32, the scalar path, partly filled last slices) and by the
+# 1024 x 2 register tile below them, with enough rows that every workgroup
+# takes several (the next row's first slice loads during the current row's
+# last).
+WIDE = [(synth.BF16, 37, 16384), (synth.BF16, 19, 32768), (synth.BF16, 9, 65536),
+        (synth.BF16, 23, 12000), (synth.F32, 21, 8192), (synth.F32, 11, 32768),
+        (synth.F32, 5, 65536), (synth.BF16, 13, 1500), (synth.BF16, 7, 9001),
+        (synth.F32, 6, 16383)]
+
+
+@pytest.mark.parametrize("mode", ["saved_rstd", "recompute", "dres"])
+@pytest.mark.parametrize("dtype,rows,H", WIDE)
+def test_bwd_wide_rows(dtype, rows, H, mode):
+    wl, x, w, dy, _, dres = _inputs(rows, H, dtype, seed=17 * rows + H, outliers=0.01)
+    x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
+    _, r64 = oracle.rmsnorm_fwd(x64, w64, wl.eps)
+    rstd32 = round_f32(r64)
+    xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
+    rstd_d = torch.from_numpy(rstd32.astype(np.float32)).to(DEV) if mode != "recompute" else None
+    dres_d = to_dev(dres, dtype) if mode == "dres" else None
+    dx = _empty(rows, H, dtype)
+    dw = torch.full((H,), float("nan"), dtype=torch_dtype(dtype), device=DEV)
+    B.rmsnorm_bwd(dyd, xd, wd, rstd_d, dres_d, dx, dw, _ws(rows, H, dtype), wl.eps)
+    torch.cuda.synchronize()
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps,
+                                  rstd=None if mode == "recompute" else rstd32,
+                                  dres=synth.to_f64(dres, dtype) if mode == "dres" else None)
     assert_output("dx", f64(dx), dxo, dtype)
     assert_dw(f64(dw), dwo, dtype)
 
