@@ -11,13 +11,12 @@ namespace rms {
 enum class DType { F32 = 0, BF16 = 1 };
 
 // Geometry chosen for a row width: a team of `team` lanes handles one row,
-// each lane holds `nch` chunks of `vec` elements.
+// each lane holds `nch` chunks of `vec` elements.  Each kernel sizes its
+// workgroups from the geometry itself.
 struct Geometry {
     int vec;
     int team;
     int nch;
-    int wg;    // workgroup size
-    int rpw;   // rows per workgroup iteration = wg / team
 };
 
 // Returns false when H needs more than the largest register tile.

@@ -34,8 +34,6 @@ bool choose_geometry(int64_t H, int vec, bool wide, Geometry* g) {
     g->vec = vec;
     g->team = team;
     g->nch = nch;
-    g->wg = team > 256 ? team : 256;
-    g->rpw = g->wg / team;
     return true;
 }
 
