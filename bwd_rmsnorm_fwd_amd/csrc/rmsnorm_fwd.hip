@@ -216,11 +216,19 @@ template <typename T, int VEC>
 static hipError_t dispatch(const FwdArgs& a, bool residual, hipStream_t s) {
     Geometry g;
     if (!choose_geometry(a.H, VEC, residual, &g)) return hipErrorInvalidValue;
+    // bf16 rows of 8193-16384 elements: 512 x 4 instead of 1024 x 2 (one row
+    // per workgroup either way).  Measured on 4096 x 16384: forward 46.9 ->
+    // 38.5 us, residual forward 92.9 -> 88.7; 512 x 8 and 512 x 16 for the
+    // wider rows and 512 x 4 for fp32 were slower.
+    if (sizeof(T) == 2 && VEC > 1 && g.team == 1024 && g.nch == 2) {
+        g.team = 512;
+        g.nch = 4;
+    }
 #define RMS_CASE(TM, NC) \
     if (g.team == TM && g.nch == NC) return launch_cfg<T, VEC, TM, NC>(a, residual, s);
     RMS_CASE(1, 1) RMS_CASE(2, 1) RMS_CASE(4, 1) RMS_CASE(8, 1) RMS_CASE(16, 1) RMS_CASE(32, 1)
     RMS_CASE(64, 1) RMS_CASE(64, 2) RMS_CASE(128, 2) RMS_CASE(256, 2) RMS_CASE(512, 1)
-    RMS_CASE(512, 2)
+    RMS_CASE(512, 2) RMS_CASE(512, 4)
     RMS_CASE(1024, 2) RMS_CASE(1024, 4) RMS_CASE(1024, 8) RMS_CASE(1024, 16)
 #undef RMS_CASE
     return hipErrorInvalidValue;

@@ -370,7 +370,7 @@ def test_rows_zero():
 GUARD = [(synth.BF16, 129, 896), (synth.BF16, 300, 128), (synth.BF16, 3, 4096),
          (synth.BF16, 1539, 4096), (synth.BF16, 5, 8192), (synth.BF16, 7, 500),
          (synth.F32, 2053, 896), (synth.F32, 5, 4095), (synth.BF16, 9, 32768),
-         (synth.F32, 5, 12289)]
+         (synth.F32, 5, 12289), (synth.BF16, 7, 16384), (synth.BF16, 3, 12000)]
 
 
 @pytest.mark.parametrize("dtype,rows,H", GUARD)
