@@ -13,8 +13,10 @@
 //   * Row pass: G persistent workgroups; rows go in blocks of R (one team
 //     per row, as in the forward) dealt round-robin to the workgroups, each
 //     prefetching its next block while finishing the current one.
-//     dy, x (and dres) are read once; rstd is the forward's saved statistic
-//     (or is recomputed from x when none is given).
+//     dy, x (and dres) are read once, through buffer resources sized to the
+//     block's rows; rstd is the forward's saved statistic (or is recomputed
+//     from x when none is given).  Rows too wide to hold in registers are
+//     streamed twice instead, one row per workgroup (bwd_rows_wide_kernel).
 //   * The row sums c (and sum x^2 when recomputing) are exact fp32 products
 //     (for bf16 inputs) accumulated in fp64, so c and r carry no cancellation
 //     error.  dx uses k = r^2 c split into two floats, k_hi + k_lo, applied

@@ -132,6 +132,36 @@ def test_bwd_multi_block(dtype, rows, H, mode):
     assert_dw(f64(dw), dwo, dtype)
 
 
+# Narrow rows in such numbers that the forward's grid (at least 4 KB of x
+# per workgroup, at least 2048 workgroups) gives every workgroup two or three
+# row blocks: the loop that loads the next block while finishing the current
+# one, and its last, partly filled block.
+MANY_BLOCKS = [(synth.BF16, 3_000_017, 1), (synth.BF16, 1_500_007, 2),
+               (synth.BF16, 700_001, 4), (synth.F32, 2_000_003, 1)]
+
+
+@pytest.mark.parametrize("dtype,rows,H", MANY_BLOCKS)
+def test_fwd_several_blocks_per_workgroup(dtype, rows, H):
+    wl, x, w, _, res, _ = _inputs(rows, H, dtype, seed=rows % 1000 + H)
+    xd, rd, wd = to_dev(x, dtype), to_dev(res, dtype), to_dev(w, dtype)
+    y = _empty(rows, H, dtype)
+    rstd = torch.full((rows,), float("nan"), device=DEV)
+    B.rmsnorm_fwd(xd, wd, y, rstd, wl.eps)
+    h, y2 = _empty(rows, H, dtype), _empty(rows, H, dtype)
+    rstd2 = torch.full((rows,), float("nan"), device=DEV)
+    B.rmsnorm_residual_fwd(xd, rd, wd, h, y2, rstd2, wl.eps)
+    torch.cuda.synchronize()
+    x64, w64 = synth.to_f64(x, dtype), synth.to_f64(w, dtype)
+    yo, ro = oracle.rmsnorm_fwd(x64, w64, wl.eps)
+    assert_output("y", f64(y), yo, dtype)
+    assert_rstd(f64(rstd), ro)
+    kind = oracle.H_BF16 if dtype == synth.BF16 else oracle.H_F32
+    ho, yo2, ro2 = oracle.rmsnorm_residual_fwd(x64, synth.to_f64(res, dtype), w64, wl.eps, kind)
+    assert np.array_equal(f64(h), ho), "h must be bit-exact"
+    assert_output("y", f64(y2), yo2, dtype)
+    assert_rstd(f64(rstd2), ro2)
+
+
 # The backward's workspace comes from the caller uninitialised.  Whatever it
 # holds (here every float of it NaN, +inf or -inf) must not reach dw, also
 # through the rows past the end of a partly filled last row block; nor may r
