@@ -386,9 +386,17 @@ def suite(path, reps=30, warmup=20):
         out.append(d)
         print(json.dumps(d), file=sys.stderr, flush=True)
 
-    for name in ["c1_f32_64x896", "c2_bf16_4096x4096", "c5a_bf16_262144x128",
-                 "c5b_bf16_8192x8192"]:
-        wl = synth.WORKLOADS[name]
+    # Rows wider than every configured workload (bf16, 128 MB per tensor):
+    # the forward's 512 x 4 tile at 16384, the backward's register tile there
+    # and its streaming kernel beyond.
+    wide = [synth.Workload(f"wide_bf16_{r}x{h}", synth.BF16, r, h, 1e-6, 701 + k, 711 + k, 721 + k,
+                           731 + k, 741 + k)
+            for k, (r, h) in enumerate(((4096, 16384), (2048, 32768), (1024, 65536)))]
+    plain = [synth.WORKLOADS[n] for n in ("c1_f32_64x896", "c2_bf16_4096x4096",
+                                          "c5a_bf16_262144x128", "c5b_bf16_8192x8192")]
+    for wl in plain + wide:
+        name = wl.name
+        is_wide = wl in wide
         sets = Sets(wl)
         C = Calls(sets, stream)
         e = sets.e
@@ -404,6 +412,10 @@ def suite(path, reps=30, warmup=20):
         emit(summarise(f"{name}/bwd", tb, bwd_bytes(wl.rows, wl.H, e), meta))
         emit(summarise(f"{name}/step_fwd_bwd", ts,
                        fwd_bytes(wl.rows, wl.H, e) + bwd_bytes(wl.rows, wl.H, e), meta))
+        if is_wide:
+            del sets, C
+            torch.cuda.empty_cache()
+            continue
         # Backward that recomputes r from x instead of reading the saved rstd
         # (4 bytes per row fewer; one more row reduction).
         (tq,) = time_calls([(C.bwd_rows(s, saved_rstd=False),) for s in sets.sets], sets.k, reps,
@@ -417,18 +429,22 @@ def suite(path, reps=30, warmup=20):
         del sets, C
         torch.cuda.empty_cache()
 
-    wl = synth.WORKLOADS["c4_bf16_residual_16384x4096"]
-    sets = Sets(wl, residual=True, dres=True)
-    C = Calls(sets, stream)
-    meta = {"workload": wl.name, "cold_sets": sets.k}
-    (tf,) = time_calls([(C.residual_fwd(s),) for s in sets.sets], sets.k, reps, warmup, stream)
-    tr, tb = time_calls([(C.bwd_rows(s, x_key="h", dres=True), C.dw_reduce(s)) for s in sets.sets],
-                        sets.k, reps, warmup, stream)
-    emit(summarise(f"{wl.name}/residual_fwd", tf, fwd_bytes(wl.rows, wl.H, 2, residual=True), meta))
-    emit(summarise(f"{wl.name}/bwd_rows_dres", tr, bwd_rows_bytes(wl.rows, wl.H, 2, dres=True), meta))
-    emit(summarise(f"{wl.name}/bwd_dres", tb, bwd_bytes(wl.rows, wl.H, 2, dres=True), meta))
-    del sets, C
-    torch.cuda.empty_cache()
+    wide_res = synth.Workload("wide_bf16_residual_2048x32768", synth.BF16, 2048, 32768, 1e-6,
+                              751, 752, 753, 754, 755, residual=True)
+    for wl in (synth.WORKLOADS["c4_bf16_residual_16384x4096"], wide_res):
+        sets = Sets(wl, residual=True, dres=True)
+        C = Calls(sets, stream)
+        meta = {"workload": wl.name, "cold_sets": sets.k}
+        (tf,) = time_calls([(C.residual_fwd(s),) for s in sets.sets], sets.k, reps, warmup, stream)
+        tr, tb = time_calls([(C.bwd_rows(s, x_key="h", dres=True), C.dw_reduce(s))
+                             for s in sets.sets], sets.k, reps, warmup, stream)
+        emit(summarise(f"{wl.name}/residual_fwd", tf, fwd_bytes(wl.rows, wl.H, 2, residual=True),
+                       meta))
+        emit(summarise(f"{wl.name}/bwd_rows_dres", tr,
+                       bwd_rows_bytes(wl.rows, wl.H, 2, dres=True), meta))
+        emit(summarise(f"{wl.name}/bwd_dres", tb, bwd_bytes(wl.rows, wl.H, 2, dres=True), meta))
+        del sets, C
+        torch.cuda.empty_cache()
 
     # Decode: 10k back-to-back calls on one stream, µs per call: from a
     # Python loop, from a loop in C, and replayed from a HIP graph.
