@@ -169,6 +169,21 @@ __device__ __forceinline__ Pack<T, VEC> buf_load_pack(BufRes r, uint32_t off) {
     return p;
 }
 
+// 16 bytes per lane from a resource straight into LDS: lane l's bytes land
+// at wave_base + 16 l (wave_base: the wavefront's own LDS region, the same
+// address in every lane).  Completion is counted by vmcnt like any load; the
+// compiler does not order a later LDS read after it, so callers wait
+// explicitly.  The body exists in the device pass only (an LDS address space
+// has no meaning in the host pass, whose kernel stubs it would otherwise
+// drop).
+template <int AUX>
+__device__ __forceinline__ void buf_load_lds16(BufRes r, void* wave_base, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)wave_base,
+                                             16, (int)off, 0, 0, AUX);
+#endif
+}
+
 __device__ __forceinline__ float buf_load_f32(BufRes r, uint32_t off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }

@@ -502,6 +502,187 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
     }
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; a field at its maximum does not wait).
+constexpr int wait_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// 1024-lane teams with two 16-byte chunks per lane (8193-16384 bf16 or
+// 4097-8192 fp32 elements): the row and a prefetched successor do not both
+// fit in registers, so each wave stages its lanes' part of the next row in
+// its own region of LDS with direct buffer-to-LDS loads while it finishes
+// the current row from registers.  The compiler does not order an LDS read
+// after the direct load that fills it, so the waits are explicit: before a
+// row is read from LDS, every memory operation older than the previous
+// row's dx stores has completed (vmcnt), and the LDS reads have returned
+// (lgkmcnt) before the region is refilled.
+// Sum over the 1024 lanes of the workgroup (16 wavefronts), every lane
+// getting the same total.  A fence before the barrier (even one restricted
+// to LDS) would wait for the staged row's direct-to-LDS loads, so the slot
+// write is waited for explicitly and the barrier stands alone, with compiler
+// barriers keeping the LDS accesses on their side; two slot sets used in
+// turn, as in team_sum_alt.
+__device__ __forceinline__ double wg_sum_lds(double v, double* slots) {
+    v = team_sum_wave<64>(v);
+    if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = v;
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's slot write is done
+    asm volatile("" ::: "memory");           // no LDS access moves across
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    double s = slots[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) s += slots[k];
+    return s;
+}
+
+template <typename T, int VEC, bool DRES>
+__global__ __launch_bounds__(1024) void bwd_rows_staged_kernel(
+    const T* dy, const T* __restrict__ x, const T* __restrict__ w,
+    const float* __restrict__ rstd, const T* dres, T* dx, float* __restrict__ partial,
+    int64_t rows, int H, int ldp, float eps) {
+    constexpr int TEAM = 1024, NCH = 2, NWT = TEAM / kWave;
+    constexpr int NT = DRES ? 3 : 2;  // row tensors staged: x, dy (, dres)
+    constexpr bool kNtLoad = DRES ? RMS_DRES_NT_LOAD != 0 : RMS_BWD_NT_LOAD != 0;
+    constexpr bool kNtStore = DRES ? RMS_DRES_NT_STORE != 0 : RMS_BWD_NT_STORE != 0;
+    constexpr int aux = kNtLoad ? kAuxNt : 0;
+    __shared__ double red[2 * 2 * NWT];
+    __shared__ __align__(16) u32x4 stage[NT][NCH][TEAM];
+    __shared__ __align__(16) u32x4 wst[NCH][TEAM];  // w, read from LDS in the loop
+
+    const int lt = threadIdx.x;
+    const int wave = lt / kWave;
+    const bool has_rstd = rstd != nullptr;
+    const double inv_h = 1.0 / (double)H;
+    const uint32_t row_bytes = (uint32_t)H * (uint32_t)sizeof(T);
+    uint32_t voff[NCH];
+    bool cok[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = (c * TEAM + lt) * VEC;
+        cok[c] = col < H;
+        voff[c] = cok[c] ? (uint32_t)col * (uint32_t)sizeof(T) : kBufOutside;
+    }
+    float acc[NCH][VEC];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[c][k] = 0.f;
+    }
+    // w goes to LDS once, so that no global load in the loop is younger than
+    // the staged row (a wait for it would wait for the staging too).
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = (c * TEAM + lt) * VEC;
+        wst[c][lt] = cok[c] ? ld128<false>(w + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    auto weights = [&](int c, float (&wc)[VEC]) {
+        Pack<T, VEC> p;
+        p.v = wst[c][lt];
+        unpack(p, wc);
+    };
+    auto lds = [&](int t, int c) { return (void*)&stage[t][c][wave * kWave]; };
+    // Stage row `row` (an empty resource past the end: nothing is read) and
+    // load its rstd; always the same NT * NCH + 1 memory operations.
+    auto stage_row = [&](int64_t row, float& rs) {
+        const bool ok = row < rows;
+        const int64_t off = ok ? row * (int64_t)H : 0;
+        const uint32_t n = ok ? row_bytes : 0u;
+        const BufRes rx = buf_rsrc(x + off, n);
+        const BufRes rdy = buf_rsrc(dy + off, n);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            buf_load_lds16<aux>(rx, lds(0, c), voff[c]);
+            buf_load_lds16<aux>(rdy, lds(1, c), voff[c]);
+            if constexpr (DRES) buf_load_lds16<aux>(buf_rsrc(dres + off, n), lds(2, c), voff[c]);
+        }
+        const BufRes rr = (has_rstd && ok) ? buf_rsrc(rstd + row, 4u) : buf_rsrc(x, 0u);
+        rs = buf_load_f32(rr, 0u);
+    };
+
+    const int64_t G = gridDim.x;
+    int64_t row = blockIdx.x;
+    float rs_next;
+    stage_row(row, rs_next);
+    int set = 0;
+    bool first = true;
+    for (; row < rows; row += G, set ^= 1) {
+        if (first) __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        else __builtin_amdgcn_s_waitcnt(wait_vm(NCH));
+        first = false;
+        Pack<T, VEC> px[NCH], pdy[NCH], pdr[DRES ? NCH : 1];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            px[c].v = stage[0][c][lt];
+            pdy[c].v = stage[1][c][lt];
+            if constexpr (DRES) pdr[c].v = stage[2][c][lt];
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        const float rs = rs_next;
+        stage_row(row + G, rs_next);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if (!cok[c]) {
+                px[c] = zero_pack<T, VEC>();
+                pdy[c] = zero_pack<T, VEC>();
+                if constexpr (DRES) pdr[c] = zero_pack<T, VEC>();
+            }
+        }
+        double cs = 0.0, ss = 0.0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            float xv[VEC], dyv[VEC], wc[VEC];
+            unpack(px[c], xv);
+            unpack(pdy[c], dyv);
+            weights(c, wc);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                cs += prod3_64(wc[k], dyv[k], xv[k], (T*)nullptr);
+                if (!has_rstd) ss += sq64(xv[k], (T*)nullptr);
+            }
+        }
+        double* slots = red + set * 2 * NWT;
+        cs = wg_sum_lds(cs, slots);
+        double r;
+        if (has_rstd) {
+            r = (double)rs;
+        } else {
+            ss = wg_sum_lds(ss, slots + NWT);
+            r = rsqrt_f64(ss * inv_h + (double)eps);
+        }
+        const RowK kq = row_k(r, cs, inv_h, true);
+        const BufRes rdx = buf_rsrc(dx + row * (int64_t)H, row_bytes);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            float xv[VEC], dyv[VEC], wc[VEC], drv[VEC], o[VEC];
+            unpack(px[c], xv);
+            unpack(pdy[c], dyv);
+            weights(c, wc);
+            if constexpr (DRES) unpack(pdr[c], drv);
+            dx_chunk<T, VEC, DRES>(xv, dyv, wc, drv, kq, o, acc[c]);
+            buf_store_vec<T, VEC, kNtStore, DRES>(rdx, voff[c], o);
+        }
+    }
+    // The loads of the row past the workgroup's last have nothing to wait
+    // for in this kernel: their resources are empty.
+    float* prow = partial + (int64_t)blockIdx.x * ldp;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = (c * TEAM + lt) * VEC;
+        if (col < H) {
+#pragma unroll
+            for (int k = 0; k < VEC; k += 4) {
+                u32x4 v;
+                v.x = __float_as_uint(acc[c][k]);
+                v.y = __float_as_uint(acc[c][k + 1]);
+                v.z = __float_as_uint(acc[c][k + 2]);
+                v.w = __float_as_uint(acc[c][k + 3]);
+                st128<false>(prow + col + k, v);
+            }
+        }
+    }
+}
+
 // dw[j] = sum_{g < G} partial[g][j] in a fixed order.  A workgroup of
 // kRedWG lanes owns kRedCols columns (kRedCL lanes x 4 columns, 128-bit
 // loads) and kRedGL lanes over g: lane gl adds rows g = gl, gl + kRedGL, ...
@@ -641,6 +822,20 @@ static hipError_t dispatch_rows(const BwdArgs& a, hipStream_t s) {
     Geometry g;
     if (!choose_geometry(a.H, VEC, a.dres != nullptr, &g)) return hipErrorInvalidValue;
     if (g.team == kWideTeam && g.nch >= 4) return launch_rows_wide<T, VEC>(a, s);
+    if constexpr (VEC > 1) {
+        if (g.team == 1024 && g.nch == 2) {
+            if (a.dres) {
+                hipLaunchKernelGGL((bwd_rows_staged_kernel<T, VEC, true>), dim3(a.G), dim3(1024), 0, s,
+                                   (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
+                                   (const T*)a.dres, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
+            } else {
+                hipLaunchKernelGGL((bwd_rows_staged_kernel<T, VEC, false>), dim3(a.G), dim3(1024), 0, s,
+                                   (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
+                                   (const T*)nullptr, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
+            }
+            return hipGetLastError();
+        }
+    }
 #define RMS_CASE(TM, NC) \
     if (g.team == TM && g.nch == NC) return launch_rows_cfg<T, VEC, TM, NC>(a, s);
     RMS_CASE(1, 1) RMS_CASE(2, 1) RMS_CASE(4, 1) RMS_CASE(8, 1) RMS_CASE(16, 1) RMS_CASE(32, 1)
