@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "librmsnorm_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["rmsnorm_api.hip", "rmsnorm_fwd.hip", "rmsnorm_bwd.hip", "rmsnorm_split.hip",
+SOURCES = ["rmsnorm_api.hip", "rmsnorm_fwd.hip", "rmsnorm_bwd.hip", "rmsnorm_bwd_wide.hip",
+           "rmsnorm_split.hip",
            "decode_gemv.hip", "decode_gemv_api.hip"]
 ARCH = "gfx950"
 
