@@ -573,13 +573,13 @@ def test_widest_rows(dtype, rows, H):
 # Rows served by the streaming backward (the geometry's 1024-lane teams with
 # 4 or more chunks per lane: 1024-lane workgroups with 4 slices, 512-lane
 # ones with 16 and 32, the scalar path, partly filled last slices) and by the
-# 1024 x 2 register tile below them, with enough rows that every workgroup
-# takes several (the next row's first slice loads during the current row's
-# last).
+# LDS-staged kernel below them (1024 x 2; 8200 bf16 and 4100 fp32 leave all
+# but one lane's second chunk past H), with enough rows that every workgroup
+# takes several (the next row loads during the current one).
 WIDE = [(synth.BF16, 37, 16384), (synth.BF16, 19, 32768), (synth.BF16, 9, 65536),
         (synth.BF16, 23, 12000), (synth.F32, 21, 8192), (synth.F32, 11, 32768),
         (synth.F32, 5, 65536), (synth.BF16, 13, 1500), (synth.BF16, 7, 9001),
-        (synth.F32, 6, 16383)]
+        (synth.F32, 6, 16383), (synth.BF16, 29, 8200), (synth.F32, 17, 4100)]
 
 
 @pytest.mark.parametrize("mode", ["saved_rstd", "recompute", "dres"])
