@@ -50,6 +50,21 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
         return col < H ? (uint32_t)col * (uint32_t)sizeof(T) : kBufOutside;
     };
     const BufRes rw = buf_rsrc(w, row_bytes);
+    // w is read in both passes of every row; up to 128 KB of it is kept in
+    // LDS (every build but fp32 at 65536), the rest re-read from L2.
+    constexpr bool kWLds = (size_t)NS * SL * sizeof(T) <= 131072;
+    __shared__ __align__(16) T wl[kWLds ? NS * SL : 1];
+    if constexpr (kWLds) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            *reinterpret_cast<Pack<T, VEC>*>(&wl[s * SL + lcol]) = buf_load_pack<T, VEC>(rw, voff(s));
+        }
+        __syncthreads();
+    }
+    auto w_slice = [&](int s, const Pack<T, VEC>& qw, float (&wc)[VEC]) {
+        if constexpr (kWLds) unpack(*reinterpret_cast<const Pack<T, VEC>*>(&wl[s * SL + lcol]), wc);
+        else unpack(qw, wc);
+    };
     float acc[NS][VEC];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -68,13 +83,13 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
         const uint32_t n = ok ? row_bytes : 0u;
         q.x = buf_load_pack<T, VEC>(buf_rsrc(x + off, n), voff(s));
         q.dy = buf_load_pack<T, VEC>(buf_rsrc(dy + off, n), voff(s));
-        q.w = buf_load_pack<T, VEC>(rw, voff(s));
+        if constexpr (!kWLds) q.w = buf_load_pack<T, VEC>(rw, voff(s));
     };
     auto load_b = [&](int64_t row, int s, Slice& q) {
         const int64_t off = row * (int64_t)H;
         q.x = buf_load_pack<T, VEC, kNtLoad>(buf_rsrc(x + off, row_bytes), voff(s));
         q.dy = buf_load_pack<T, VEC, kNtLoad>(buf_rsrc(dy + off, row_bytes), voff(s));
-        q.w = buf_load_pack<T, VEC>(rw, voff(s));
+        if constexpr (!kWLds) q.w = buf_load_pack<T, VEC>(rw, voff(s));
         if constexpr (DRES) q.dr = buf_load_pack<T, VEC, kNtLoad>(buf_rsrc(dres + off, row_bytes), voff(s));
     };
 
@@ -95,7 +110,7 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
             float xv[VEC], dyv[VEC], wc[VEC];
             unpack(q.x, xv);
             unpack(q.dy, dyv);
-            unpack(q.w, wc);
+            w_slice(s, q.w, wc);
 #pragma unroll
             for (int k = 0; k < VEC; ++k) {
                 cs += prod3_64(wc[k], dyv[k], xv[k], (T*)nullptr);
@@ -126,7 +141,7 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
             float xv[VEC], dyv[VEC], wc[VEC], drv[VEC], o[VEC];
             unpack(q.x, xv);
             unpack(q.dy, dyv);
-            unpack(q.w, wc);
+            w_slice(s, q.w, wc);
             if constexpr (DRES) unpack(q.dr, drv);
             dx_chunk<T, VEC, DRES>(xv, dyv, wc, drv, kq, o, acc[s]);
             buf_store_vec<T, VEC, kNtStore, DRES>(rdx, voff(s), o);
