@@ -78,4 +78,126 @@ __device__ __forceinline__ void dx_chunk(const float (&xv)[VEC], const float (&d
     }
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; a field at its maximum does not wait).
+constexpr int wait_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// Sum over a team of TEAM lanes for kernels with direct-to-LDS loads in
+// flight.  A fence before the barrier (even one restricted to LDS) would
+// wait for those loads, so the slot write is waited for explicitly and the
+// barrier stands alone, with compiler barriers keeping the LDS accesses on
+// their side.  Slots as in team_sum_alt (callers alternate two sets).
+template <int TEAM, typename V>
+__device__ __forceinline__ V team_sum_nofence(V v, V* lds) {
+    if constexpr (TEAM <= 64) {
+        return team_sum_wave<TEAM>(v);
+    } else {
+        constexpr int NW = TEAM / kWave;
+        v = team_sum_wave<64>(v);
+        const int lt = threadIdx.x % TEAM;
+        V* slot = lds + (threadIdx.x / TEAM) * NW;
+        if ((lt & (kWave - 1)) == 0) slot[lt / kWave] = v;
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's slot write is done
+        asm volatile("" ::: "memory");           // no LDS access moves across
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        V s = slot[0];
+#pragma unroll
+        for (int k = 1; k < NW; ++k) s += slot[k];
+        return s;
+    }
+}
+
+// The workgroup's dw partial row from the column sums of its R = WG / TEAM
+// teams (lane lt of a team holds columns (c * TEAM + lt) * VEC + k).  The
+// teams are combined in team order through comb: side by side ([R][HT],
+// summed per column) when that fits in 32 KiB, else one after another into
+// a single [HT] row.  With VEC > 1, H is a multiple of VEC, so groups of four
+// columns that start below H end below H (and below HT); ldp is a multiple
+// of 64.
+template <int VEC, int TEAM, int NCH, int WG>
+struct PartialComb {
+    static constexpr int R = WG / TEAM;
+    static constexpr int HT = TEAM * NCH * VEC;  // columns covered by one team
+    static constexpr bool kWide = R > 1 && R * HT <= 8192;
+    static constexpr int kFloats = R == 1 ? 1 : (kWide ? R * HT : HT);  // comb size
+};
+
+template <int VEC, int TEAM, int NCH, int WG>
+__device__ __forceinline__ void write_partial(const float (&acc)[NCH][VEC], float* comb,
+                                              float* prow, int H) {
+    using PC = PartialComb<VEC, TEAM, NCH, WG>;
+    constexpr int R = PC::R, HT = PC::HT;
+    const int tid = threadIdx.x;
+    const int team = tid / TEAM;
+    const int lt = tid % TEAM;
+    auto store4 = [&](int col, float a, float b, float c, float d) {
+        u32x4 v;
+        v.x = __float_as_uint(a); v.y = __float_as_uint(b);
+        v.z = __float_as_uint(c); v.w = __float_as_uint(d);
+        st128<false>(prow + col, v);
+    };
+    if constexpr (R == 1) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int col = (c * TEAM + lt) * VEC;
+            if (col < H) {
+                if constexpr (VEC == 1) {
+                    prow[col] = acc[c][0];
+                } else {
+#pragma unroll
+                    for (int k = 0; k < VEC; k += 4)
+                        store4(col + k, acc[c][k], acc[c][k + 1], acc[c][k + 2], acc[c][k + 3]);
+                }
+            }
+        }
+    } else if constexpr (PC::kWide) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) comb[team * HT + (c * TEAM + lt) * VEC + k] = acc[c][k];
+        }
+        __syncthreads();
+        if constexpr (VEC >= 4) {
+            for (int col = tid * 4; col < H; col += WG * 4) {
+                float4 sum = *reinterpret_cast<const float4*>(comb + col);
+                for (int t = 1; t < R; ++t) {
+                    const float4 v = *reinterpret_cast<const float4*>(comb + t * HT + col);
+                    sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+                }
+                store4(col, sum.x, sum.y, sum.z, sum.w);
+            }
+        } else {
+            for (int col = tid; col < H && col < HT; col += WG) {
+                float sum = comb[col];
+                for (int t = 1; t < R; ++t) sum += comb[t * HT + col];
+                prow[col] = sum;
+            }
+        }
+    } else {
+        for (int t = 0; t < R; ++t) {
+            if (team == t) {
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) {
+                        const int col = (c * TEAM + lt) * VEC + k;
+                        comb[col] = (t == 0) ? acc[c][k] : comb[col] + acc[c][k];
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        if constexpr (VEC >= 4) {
+            for (int col = tid * 4; col < H; col += WG * 4) {
+                const float4 v = *reinterpret_cast<const float4*>(comb + col);
+                store4(col, v.x, v.y, v.z, v.w);
+            }
+        } else {
+            for (int col = tid; col < H && col < HT; col += WG) prow[col] = comb[col];
+        }
+    }
+}
+
 }  // namespace rms

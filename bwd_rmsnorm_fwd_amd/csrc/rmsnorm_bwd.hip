@@ -48,7 +48,6 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
                                                       int H, int ldp, float eps) {
     constexpr int R = WG / TEAM;
     constexpr int NWT = TEAM > kWave ? TEAM / kWave : 1;
-    constexpr int HT = TEAM * NCH * VEC;  // columns covered by one team
     constexpr int EB = NCH * VEC * (int)sizeof(T);  // bytes per lane per row tensor
     // Register budget: w cached and the next rows prefetched unless the
     // per-lane tile is large for this workgroup size.
@@ -56,15 +55,11 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
     constexpr bool kPrefetch = RMS_BWD_PREFETCH != 0 && EB * WG <= 16384;
     constexpr bool kNtLoad = DRES ? RMS_DRES_NT_LOAD != 0 : RMS_BWD_NT_LOAD != 0;
     constexpr bool kNtStore = DRES ? RMS_DRES_NT_STORE != 0 : RMS_BWD_NT_STORE != 0;
-    // Teams combine their dw sums either side by side ([R][HT], summed per
-    // column in team order) when that fits in 32 KiB, or one after another
-    // into a single [HT] row.
-    constexpr bool kWideComb = R > 1 && R * HT <= 8192;
     // Row-sum slots: two sets used in turn (one barrier per sum), each
     // with room for c and, when recomputing r, sum x^2.
     constexpr int kRedSet = 2 * R * NWT;
     __shared__ double red[TEAM > kWave ? 2 * kRedSet : 1];
-    __shared__ __align__(16) float comb[R == 1 ? 1 : (kWideComb ? R * HT : HT)];
+    __shared__ __align__(16) float comb[PartialComb<VEC, TEAM, NCH, WG>::kFloats];
 
     const int tid = threadIdx.x;
     const int team = tid / TEAM;
@@ -218,76 +213,8 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
             set ^= 1;
         }
     }
-    // One partial row per workgroup: combine the R teams in team order.
-    // With VEC > 1, H is a multiple of VEC, so groups of four columns that
-    // start below H end below H (and below HT); ldp is a multiple of 64.
-    float* prow = partial + (int64_t)blockIdx.x * ldp;
-    auto store4 = [&](int col, float a, float b, float c, float d) {
-        u32x4 v;
-        v.x = __float_as_uint(a); v.y = __float_as_uint(b);
-        v.z = __float_as_uint(c); v.w = __float_as_uint(d);
-        st128<false>(prow + col, v);
-    };
-    if constexpr (R == 1) {
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int col = (c * TEAM + lt) * VEC;
-            if (col < H) {
-                if constexpr (VEC == 1) {
-                    prow[col] = acc[c][0];
-                } else {
-#pragma unroll
-                    for (int k = 0; k < VEC; k += 4)
-                        store4(col + k, acc[c][k], acc[c][k + 1], acc[c][k + 2], acc[c][k + 3]);
-                }
-            }
-        }
-    } else if constexpr (kWideComb) {
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) comb[team * HT + (c * TEAM + lt) * VEC + k] = acc[c][k];
-        }
-        __syncthreads();
-        if constexpr (VEC >= 4) {
-            for (int col = tid * 4; col < H; col += WG * 4) {
-                float4 sum = *reinterpret_cast<const float4*>(comb + col);
-                for (int t = 1; t < R; ++t) {
-                    const float4 v = *reinterpret_cast<const float4*>(comb + t * HT + col);
-                    sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
-                }
-                store4(col, sum.x, sum.y, sum.z, sum.w);
-            }
-        } else {
-            for (int col = tid; col < H && col < HT; col += WG) {
-                float sum = comb[col];
-                for (int t = 1; t < R; ++t) sum += comb[t * HT + col];
-                prow[col] = sum;
-            }
-        }
-    } else {
-        for (int t = 0; t < R; ++t) {
-            if (team == t) {
-#pragma unroll
-                for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-                    for (int k = 0; k < VEC; ++k) {
-                        const int col = (c * TEAM + lt) * VEC + k;
-                        comb[col] = (t == 0) ? acc[c][k] : comb[col] + acc[c][k];
-                    }
-                }
-            }
-            __syncthreads();
-        }
-        if constexpr (VEC >= 4) {
-            for (int col = tid * 4; col < H; col += WG * 4) {
-                const float4 v = *reinterpret_cast<const float4*>(comb + col);
-                store4(col, v.x, v.y, v.z, v.w);
-            }
-        } else {
-            for (int col = tid; col < H && col < HT; col += WG) prow[col] = comb[col];
-        }
-    }
+    // One partial row per workgroup: the R teams combined in team order.
+    write_partial<VEC, TEAM, NCH, WG>(acc, comb, partial + (int64_t)blockIdx.x * ldp, H);
 }
 
 // dw[j] = sum_{g < G} partial[g][j] in a fixed order.  A workgroup of

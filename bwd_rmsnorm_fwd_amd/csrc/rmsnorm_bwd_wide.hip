@@ -171,11 +171,6 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
     }
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8; a field at its maximum does not wait).
-constexpr int wait_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
-constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
-
 // 1024-lane teams with two 16-byte chunks per lane (8193-16384 bf16 or
 // 4097-8192 fp32 elements): the row and a prefetched successor do not both
 // fit in registers, so each wave stages its lanes' part of the next row in
@@ -185,25 +180,6 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 // row is read from LDS, every memory operation older than the previous
 // row's dx stores has completed (vmcnt), and the LDS reads have returned
 // (lgkmcnt) before the region is refilled.
-// Sum over the 1024 lanes of the workgroup (16 wavefronts), every lane
-// getting the same total.  A fence before the barrier (even one restricted
-// to LDS) would wait for the staged row's direct-to-LDS loads, so the slot
-// write is waited for explicitly and the barrier stands alone, with compiler
-// barriers keeping the LDS accesses on their side; two slot sets used in
-// turn, as in team_sum_alt.
-__device__ __forceinline__ double wg_sum_lds(double v, double* slots) {
-    v = team_sum_wave<64>(v);
-    if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = v;
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's slot write is done
-    asm volatile("" ::: "memory");           // no LDS access moves across
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    double s = slots[0];
-#pragma unroll
-    for (int k = 1; k < 16; ++k) s += slots[k];
-    return s;
-}
-
 template <typename T, int VEC, bool DRES>
 __global__ __launch_bounds__(1024) void bwd_rows_staged_kernel(
     const T* dy, const T* __restrict__ x, const T* __restrict__ w,
@@ -311,12 +287,12 @@ __global__ __launch_bounds__(1024) void bwd_rows_staged_kernel(
             }
         }
         double* slots = red + set * 2 * NWT;
-        cs = wg_sum_lds(cs, slots);
+        cs = team_sum_nofence<1024>(cs, slots);
         double r;
         if (has_rstd) {
             r = (double)rs;
         } else {
-            ss = wg_sum_lds(ss, slots + NWT);
+            ss = team_sum_nofence<1024>(ss, slots + NWT);
             r = rsqrt_f64(ss * inv_h + (double)eps);
         }
         const RowK kq = row_k(r, cs, inv_h, true);
@@ -332,8 +308,10 @@ __global__ __launch_bounds__(1024) void bwd_rows_staged_kernel(
             buf_store_vec<T, VEC, kNtStore, DRES>(rdx, voff[c], o);
         }
     }
-    // The loads of the row past the workgroup's last have nothing to wait
-    // for in this kernel: their resources are empty.
+    // The loads staged past the workgroup's last row read nothing (their
+    // resources are empty), but they still write LDS: wait for them before
+    // the workgroup can end and its LDS go to another.
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
     float* prow = partial + (int64_t)blockIdx.x * ldp;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
