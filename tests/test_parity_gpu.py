@@ -582,8 +582,14 @@ WIDE = [(synth.BF16, 37, 16384), (synth.BF16, 19, 32768), (synth.BF16, 9, 65536)
         (synth.F32, 6, 16383), (synth.BF16, 29, 8200), (synth.F32, 17, 4100)]
 
 
+# More rows than workgroups, so that each workgroup of the LDS-staged and
+# streaming kernels carries its prefetch across several rows.
+WIDE_MULTI = [(synth.BF16, 600, 12288), (synth.BF16, 520, 24576), (synth.BF16, 300, 65536),
+              (synth.F32, 530, 6144), (synth.F32, 300, 20000)]
+
+
 @pytest.mark.parametrize("mode", ["saved_rstd", "recompute", "dres"])
-@pytest.mark.parametrize("dtype,rows,H", WIDE)
+@pytest.mark.parametrize("dtype,rows,H", WIDE + WIDE_MULTI)
 def test_bwd_wide_rows(dtype, rows, H, mode):
     wl, x, w, dy, _, dres = _inputs(rows, H, dtype, seed=17 * rows + H, outliers=0.01)
     x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
