@@ -6,8 +6,16 @@
 //
 // P1 = "训推加速 Qwen3 实战：从“调包”到手写 Triton Kernel（含 backward）":
 //   §5.3 the backward formulas; §5.4 dw in two passes rather than atomics.
+#include <utility>
+
 #include "bwd_row_math.hpp"
 #include "launch.hpp"
+
+// 1: rows of 1024-lane teams with four 16-byte chunks per lane and no
+// residual-stream gradient are held in LDS (bwd_rows_ldsrow_kernel).
+#ifndef RMS_BWD_LDSROW
+#define RMS_BWD_LDSROW 1
+#endif
 
 namespace rms {
 
@@ -330,6 +338,211 @@ __global__ __launch_bounds__(1024) void bwd_rows_staged_kernel(
     }
 }
 
+// LDS byte address of a __shared__ object (device pass only).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+#else
+    (void)p;
+    return 0u;
+#endif
+}
+
+// Two 16-byte LDS reads at a + OFF and b + OFF with their lgkmcnt wait, in
+// one asm statement.  Read as ordinary LDS loads, regions that direct loads
+// fill make the compiler wait first for every direct load in flight (it
+// cannot tell the regions apart), which would drain the loads of the chunks
+// still to come.
+template <int OFF>
+__device__ __forceinline__ void lds_read2(uint32_t a, uint32_t b, u32x4& va, u32x4& vb) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    asm volatile(
+        "ds_read_b128 %0, %2 offset:%4\n\t"
+        "ds_read_b128 %1, %3 offset:%4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(va), "=&v"(vb)
+        : "v"(a), "v"(b), "i"(OFF)
+        : "memory");
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), in order.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Rows of 16385-32768 bf16 or 8193-16384 fp32 elements (WG lanes with NCH
+// 16-byte chunks each, 512 x 8), without a residual-stream gradient: one row
+// at a time, its x and dy held in LDS (128 KB), so that pass B reads them from
+// LDS instead of again from the caches.  Each wave stages its lanes' part of
+// every chunk in its own LDS region with direct buffer-to-LDS loads; pass A
+// waits for each chunk as it is summed, and pass B, after reading chunk c
+// back, refills that region with chunk c of the workgroup's next row.  w
+// stays in registers (512 lanes leave room for it beside the dw sums).
+// Chunk c of a row is addressed through a resource that starts at the chunk
+// and ends at the row's end, so one lane offset serves every chunk and lanes
+// past H read zeros.  The compiler does not order an LDS read after the
+// direct load that fills it, so the waits are explicit; vmcnt counts the
+// loads, direct loads and stores of a wave in issue order:
+//   * the first row and w are waited for in full before the loop (so the
+//     compiler, too, knows that w has landed and adds no wait for it);
+//   * a later row's chunk c was staged in the previous row's pass B, which
+//     issues per chunk its two loads and then its dx store: 1 + 3 (NCH - 1 - c)
+//     operations are younger.
+template <int NCH, int C>
+__device__ __forceinline__ void wait_chunk() {
+    __builtin_amdgcn_s_waitcnt(wait_vm(1 + 3 * (NCH - 1 - C)));
+    asm volatile("" ::: "memory");
+}
+
+template <typename T, int VEC, int WG, int NCH>
+__global__ __launch_bounds__(WG) void bwd_rows_ldsrow_kernel(
+    const T* dy, const T* __restrict__ x, const T* __restrict__ w,
+    const float* __restrict__ rstd, T* dx, float* __restrict__ partial, int64_t rows, int H,
+    int ldp, float eps) {
+    constexpr int NWT = WG / kWave;
+    static_assert(3 * NCH <= 63, "vmcnt range");
+    constexpr bool kNtLoad = RMS_BWD_NT_LOAD != 0;
+    constexpr bool kNtStore = RMS_BWD_NT_STORE != 0;
+    constexpr int aux = kNtLoad ? kAuxNt : 0;
+    constexpr int kChunkElems = WG * VEC;               // elements per chunk
+    constexpr uint32_t kChunkBytes = kChunkElems * sizeof(T);
+    constexpr uint32_t kLdsChunk = WG * 16;             // LDS bytes per chunk
+    __shared__ double red[2 * 2 * NWT];
+    __shared__ __align__(16) u32x4 stage[2][NCH][WG];  // x, dy of the current row
+
+    const int lt = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(lt / kWave);
+    const bool has_rstd = rstd != nullptr;
+    const double inv_h = 1.0 / (double)H;
+    const uint32_t row_bytes = (uint32_t)H * (uint32_t)sizeof(T);
+    const uint32_t loff = (uint32_t)lt * VEC * (uint32_t)sizeof(T);  // lane offset in a chunk
+    // Bytes of the row from chunk c on (0 past the row).  Uniform, and kept
+    // in scalar registers: formed as a vector saturating subtract, a
+    // resource size would make the compiler loop over lanes at every load.
+    auto rest = [&](int c, uint32_t n) {
+        return (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(n > c * kChunkBytes ? n - c * kChunkBytes : 0u));
+    };
+    Pack<T, VEC> wp[NCH];
+    static_for<NCH>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        wp[c] = buf_load_pack<T, VEC>(buf_rsrc(w + c * kChunkElems, rest(c, row_bytes)), loff);
+    });
+    float acc[NCH][VEC];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[c][k] = 0.f;
+    }
+    // Chunk c of row `row` (past the end: empty resources, nothing is read):
+    // two direct loads.
+    auto stage_chunk = [&](int64_t row, int c) {
+        const bool ok = row < rows;
+        const int64_t off = (ok ? row * (int64_t)H : 0) + c * kChunkElems;
+        const uint32_t n = ok ? rest(c, row_bytes) : 0u;
+        buf_load_lds16<aux>(buf_rsrc(x + off, n), &stage[0][c][wave * kWave], loff);
+        buf_load_lds16<aux>(buf_rsrc(dy + off, n), &stage[1][c][wave * kWave], loff);
+    };
+    auto load_rs = [&](int64_t row) {
+        const BufRes rr = (has_rstd && row < rows) ? buf_rsrc(rstd + row, 4u) : buf_rsrc(x, 0u);
+        return buf_load_f32(rr, 0u);
+    };
+    const uint32_t ax = lds_addr(&stage[0][0][lt]);
+    const uint32_t ady = lds_addr(&stage[1][0][lt]);
+    // Chunk c as read back; lanes past H get zeros (the region may hold an
+    // earlier row's bytes there).
+    auto read_chunk = [&](auto cc, Pack<T, VEC>& px, Pack<T, VEC>& pdy) {
+        constexpr int c = decltype(cc)::value;
+        lds_read2<c * kLdsChunk>(ax, ady, px.v, pdy.v);
+        if (loff + c * kChunkBytes >= row_bytes) {
+            px = zero_pack<T, VEC>();
+            pdy = zero_pack<T, VEC>();
+        }
+    };
+
+    const int64_t G = gridDim.x;
+    int64_t row = blockIdx.x;
+    float rs = load_rs(row);
+    for (int c = 0; c < NCH; ++c) stage_chunk(row, c);
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    asm volatile("" ::: "memory");
+    int set = 0;
+    for (; row < rows; row += G, set ^= 1) {
+        // w stays packed between rows: an empty asm that "changes" it keeps
+        // the compiler from hoisting its unpacked floats out of the loop.
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) asm volatile("" : "+v"(wp[c].v));
+        // Pass A: the row sums, each chunk as soon as it has landed.
+        double cs = 0.0, ss = 0.0;
+        static_for<NCH>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            wait_chunk<NCH, c>();
+            Pack<T, VEC> px, pdy;
+            read_chunk(cc, px, pdy);
+            float xv[VEC], dyv[VEC], wc[VEC];
+            unpack(px, xv);
+            unpack(pdy, dyv);
+            unpack(wp[c], wc);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                cs += prod3_64(wc[k], dyv[k], xv[k], (T*)nullptr);
+                if (!has_rstd) ss += sq64(xv[k], (T*)nullptr);
+            }
+        });
+        double* slots = red + set * 2 * NWT;
+        cs = team_sum_nofence<WG>(cs, slots);
+        double r;
+        if (has_rstd) {
+            r = (double)rs;
+        } else {
+            ss = team_sum_nofence<WG>(ss, slots + NWT);
+            r = rsqrt_f64(ss * inv_h + (double)eps);
+        }
+        const RowK kq = row_k(r, cs, inv_h, true);
+        rs = load_rs(row + G);
+        // Pass B: dx and the dw terms from the chunks in LDS; each chunk's
+        // region is refilled with the next row's chunk once read.
+        T* const dxr = dx + row * (int64_t)H;
+        static_for<NCH>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            Pack<T, VEC> px, pdy;
+            read_chunk(cc, px, pdy);
+            stage_chunk(row + G, c);
+            float xv[VEC], dyv[VEC], wc[VEC], drv[VEC], o[VEC];
+            unpack(px, xv);
+            unpack(pdy, dyv);
+            unpack(wp[c], wc);
+            dx_chunk<T, VEC, false>(xv, dyv, wc, drv, kq, o, acc[c]);
+            buf_store_vec<T, VEC, kNtStore>(buf_rsrc(dxr + c * kChunkElems, rest(c, row_bytes)),
+                                            loff, o);
+        });
+    }
+    // The chunks staged past the workgroup's last row read nothing but still
+    // write LDS: wait for them before the workgroup can end.
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    float* prow = partial + (int64_t)blockIdx.x * ldp;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = c * kChunkElems + lt * VEC;
+        if (col < H) {
+#pragma unroll
+            for (int k = 0; k < VEC; k += 4) {
+                u32x4 v;
+                v.x = __float_as_uint(acc[c][k]);
+                v.y = __float_as_uint(acc[c][k + 1]);
+                v.z = __float_as_uint(acc[c][k + 2]);
+                v.w = __float_as_uint(acc[c][k + 3]);
+                st128<false>(prow + col + k, v);
+            }
+        }
+    }
+}
+
 // Rows the geometry table gives a 1024-lane team with 4 or more chunks per
 // lane (wider than 16384 bf16 or 8192 fp32 elements with 128-bit access,
 // 2048 with scalar access): the streaming kernel, in 1024-lane workgroups
@@ -354,6 +567,14 @@ static hipError_t launch_wide_cfg(const BwdArgs& a, hipStream_t s) {
 template <typename T, int VEC>
 static hipError_t launch_rows_wide(const BwdArgs& a, hipStream_t s) {
     const int64_t n1024 = (a.H + 1024 * VEC - 1) / (1024 * VEC);
+    if constexpr (VEC > 1 && RMS_BWD_LDSROW) {
+        if (n1024 <= 4 && !a.dres) {
+            hipLaunchKernelGGL((bwd_rows_ldsrow_kernel<T, VEC, 512, 8>), dim3(a.G), dim3(512), 0, s,
+                               (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd, (T*)a.dx,
+                               a.partial, a.rows, a.H, a.ldp, a.eps);
+            return hipGetLastError();
+        }
+    }
     if (n1024 <= 4) return launch_wide_cfg<T, VEC, 1024, 4>(a, s);
     const int64_t n512 = (a.H + 512 * VEC - 1) / (512 * VEC);
     if (n512 <= 16) return launch_wide_cfg<T, VEC, 512, 16>(a, s);

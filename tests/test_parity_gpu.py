@@ -585,7 +585,8 @@ WIDE = [(synth.BF16, 37, 16384), (synth.BF16, 19, 32768), (synth.BF16, 9, 65536)
 # More rows than workgroups, so that each workgroup of the LDS-staged and
 # streaming kernels carries its prefetch across several rows.
 WIDE_MULTI = [(synth.BF16, 600, 12288), (synth.BF16, 520, 24576), (synth.BF16, 300, 65536),
-              (synth.F32, 530, 6144), (synth.F32, 300, 20000)]
+              (synth.F32, 530, 6144), (synth.F32, 300, 20000), (synth.F32, 290, 12288),
+              (synth.BF16, 270, 20000), (synth.BF16, 3, 32760), (synth.F32, 260, 16384)]
 
 
 @pytest.mark.parametrize("mode", ["saved_rstd", "recompute", "dres"])
