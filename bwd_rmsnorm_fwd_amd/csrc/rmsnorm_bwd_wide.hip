@@ -49,15 +49,19 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
     const bool has_rstd = rstd != nullptr;
     const double inv_h = 1.0 / (double)H;
     const uint32_t row_bytes = (uint32_t)H * (uint32_t)sizeof(T);
-    // The lane's offset in slice s; chunks past H (and slices past the row)
-    // read zeros and are not stored.  Formed when used rather than kept: the
-    // registers go to the dw sums.
+    // Slice s of a row is addressed through a resource that starts at the
+    // slice and ends at the row's end, so one lane offset serves every slice
+    // and lanes past H read zeros and store nothing.  The sizes are made
+    // uniform explicitly (as a vector saturating subtract they would turn
+    // every access into a loop over lanes).
     const int lcol = lt * VEC;
-    auto voff = [&](int s) -> uint32_t {
-        const int col = s * SL + lcol;
-        return col < H ? (uint32_t)col * (uint32_t)sizeof(T) : kBufOutside;
+    const uint32_t loff = (uint32_t)lcol * (uint32_t)sizeof(T);
+    constexpr uint32_t SLB = SL * sizeof(T);
+    auto sres = [&](const T* rowp, int s, uint32_t n) {
+        const uint32_t rest = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(n > s * SLB ? n - s * SLB : 0u));
+        return buf_rsrc(rowp + s * SL, rest);
     };
-    const BufRes rw = buf_rsrc(w, row_bytes);
     // w is read in both passes of every row; up to 128 KB of it is kept in
     // LDS (every build but fp32 at 65536), the rest re-read from L2.
     constexpr bool kWLds = (size_t)NS * SL * sizeof(T) <= 131072;
@@ -65,7 +69,8 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
     if constexpr (kWLds) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            *reinterpret_cast<Pack<T, VEC>*>(&wl[s * SL + lcol]) = buf_load_pack<T, VEC>(rw, voff(s));
+            *reinterpret_cast<Pack<T, VEC>*>(&wl[s * SL + lcol]) =
+                buf_load_pack<T, VEC>(sres(w, s, row_bytes), loff);
         }
         __syncthreads();
     }
@@ -89,16 +94,16 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
         const bool ok = row < rows;
         const int64_t off = ok ? row * (int64_t)H : 0;
         const uint32_t n = ok ? row_bytes : 0u;
-        q.x = buf_load_pack<T, VEC>(buf_rsrc(x + off, n), voff(s));
-        q.dy = buf_load_pack<T, VEC>(buf_rsrc(dy + off, n), voff(s));
-        if constexpr (!kWLds) q.w = buf_load_pack<T, VEC>(rw, voff(s));
+        q.x = buf_load_pack<T, VEC>(sres(x + off, s, n), loff);
+        q.dy = buf_load_pack<T, VEC>(sres(dy + off, s, n), loff);
+        if constexpr (!kWLds) q.w = buf_load_pack<T, VEC>(sres(w, s, row_bytes), loff);
     };
     auto load_b = [&](int64_t row, int s, Slice& q) {
         const int64_t off = row * (int64_t)H;
-        q.x = buf_load_pack<T, VEC, kNtLoad>(buf_rsrc(x + off, row_bytes), voff(s));
-        q.dy = buf_load_pack<T, VEC, kNtLoad>(buf_rsrc(dy + off, row_bytes), voff(s));
-        if constexpr (!kWLds) q.w = buf_load_pack<T, VEC>(rw, voff(s));
-        if constexpr (DRES) q.dr = buf_load_pack<T, VEC, kNtLoad>(buf_rsrc(dres + off, row_bytes), voff(s));
+        q.x = buf_load_pack<T, VEC, kNtLoad>(sres(x + off, s, row_bytes), loff);
+        q.dy = buf_load_pack<T, VEC, kNtLoad>(sres(dy + off, s, row_bytes), loff);
+        if constexpr (!kWLds) q.w = buf_load_pack<T, VEC>(sres(w, s, row_bytes), loff);
+        if constexpr (DRES) q.dr = buf_load_pack<T, VEC, kNtLoad>(sres(dres + off, s, row_bytes), loff);
     };
 
     const int64_t G = gridDim.x;
@@ -107,6 +112,10 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
     int64_t row = blockIdx.x;
     load_a(row, 0, buf[0]);
     for (; row < rows; row += G, set ^= 1) {
+        // The w slices are read from LDS where they are used: without this
+        // compiler barrier they would be hoisted out of the loop, into
+        // registers the dw sums need.
+        asm volatile("" ::: "memory");
         // Pass A: the row sums, slice s while slice s + 1 loads (after the
         // last slice, pass B's first).
         double cs = 0.0, ss = 0.0;
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
         const RowK kq = row_k(r, cs, inv_h, true);
         // Pass B: dx and the dw terms, slice s while slice s + 1 loads
         // (after the last slice, the next row's first).
-        const BufRes rdx = buf_rsrc(dx + row * (int64_t)H, row_bytes);
+        T* const dxr = dx + row * (int64_t)H;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             if (s + 1 < NS) load_b(row, s + 1, buf[(s + 1) & 1]);
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
             w_slice(s, q.w, wc);
             if constexpr (DRES) unpack(q.dr, drv);
             dx_chunk<T, VEC, DRES>(xv, dyv, wc, drv, kq, o, acc[s]);
-            buf_store_vec<T, VEC, kNtStore, DRES>(rdx, voff(s), o);
+            buf_store_vec<T, VEC, kNtStore, DRES>(sres(dxr, s, row_bytes), loff, o);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
