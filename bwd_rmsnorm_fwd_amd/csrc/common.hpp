@@ -181,6 +181,10 @@ __device__ __forceinline__ void buf_load_lds16(BufRes r, void* wave_base, uint32
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)wave_base,
                                              16, (int)off, 0, 0, AUX);
+#else
+    (void)r;
+    (void)wave_base;
+    (void)off;
 #endif
 }
 
