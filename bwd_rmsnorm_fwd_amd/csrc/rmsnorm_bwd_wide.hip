@@ -112,10 +112,6 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
     int64_t row = blockIdx.x;
     load_a(row, 0, buf[0]);
     for (; row < rows; row += G, set ^= 1) {
-        // The w slices are read from LDS where they are used: without this
-        // compiler barrier they would be hoisted out of the loop, into
-        // registers the dw sums need.
-        asm volatile("" ::: "memory");
         // Pass A: the row sums, slice s while slice s + 1 loads (after the
         // last slice, pass B's first).
         double cs = 0.0, ss = 0.0;
