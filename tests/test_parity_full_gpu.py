@@ -116,17 +116,22 @@ def test_workload_decode_splitrow(splits):
     assert np.max(np.abs(f64(y) - f64(y_plain))) <= np.max(np.abs(yo)) * 2.0 ** -7
 
 
-def test_beyond_2_31_elements():
-    """Tensors of 2^31 + 12288 bf16 elements (524291 rows of 4096): every
+# (block rows P, H): the register tile, the LDS-staged and the row-in-LDS
+# backward kernels.  P divides neither the row count nor 2^31 / H.
+BEYOND = [(4099, 4096), (1031, 12288), (257, 32768)]
+
+
+@pytest.mark.parametrize("P,H", BEYOND)
+def test_beyond_2_31_elements(P, H):
+    """Tensors of just over 2^31 bf16 elements (2^31 / H + 3 rows): every
     offset past 2^31 elements (2^32 bytes) must reach its own row.  The input
-    is a seeded block of 4099 rows tiled on the device; 524288 rows (2^31
-    elements) is not a multiple of 4099, so an index that wrapped would read a
-    row holding other values.  The block's outputs are checked against the
-    oracle, and every row of the large run must equal its block row bitwise
-    (row outputs do not depend on the rest of the batch); dw is checked
-    against the oracle with dy scaled by each block row's repeat count (dw is
-    linear in dy)."""
-    P, H, rows = 4099, 4096, (1 << 19) + 3
+    is a seeded block of P rows tiled on the device; 2^31 / H rows is not a
+    multiple of P, so an index that wrapped would read a row holding other
+    values.  The block's outputs are checked against the oracle, and every
+    row of the large run must equal its block row bitwise (row outputs do not
+    depend on the rest of the batch); dw is checked against the oracle with dy
+    scaled by each block row's repeat count (dw is linear in dy)."""
+    rows = (1 << 31) // H + 3
     dt = synth.BF16
     wl = synth.small_case(P, H, dt, seed=31, residual=True)
     x, w, dy, res = wl.x(), wl.w(), wl.dy(), wl.res()
