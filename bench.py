@@ -375,6 +375,27 @@ def summarise(name, us, nbytes, extra=None):
     return d
 
 
+def wide_workloads():
+    """Rows wider than every configured workload (bf16, 128 MB per tensor):
+    the forward's 512 x 4 tile at 16384, the backward's register tile there,
+    its row-in-LDS kernel at 32768 and its streaming kernel at 65536 and with
+    a residual-stream gradient at 32768."""
+    from bwd_rmsnorm_fwd_amd import synth
+    wide = [synth.Workload(f"wide_bf16_{r}x{h}", synth.BF16, r, h, 1e-6, 701 + k, 711 + k, 721 + k,
+                           731 + k, 741 + k)
+            for k, (r, h) in enumerate(((4096, 16384), (2048, 32768), (1024, 65536)))]
+    wide.append(synth.Workload("wide_bf16_residual_2048x32768", synth.BF16, 2048, 32768, 1e-6,
+                               751, 752, 753, 754, 755, residual=True))
+    return wide
+
+
+def workload_by_name(name):
+    from bwd_rmsnorm_fwd_amd import synth
+    if name in synth.WORKLOADS:
+        return synth.WORKLOADS[name]
+    return {w.name: w for w in wide_workloads()}[name]
+
+
 def suite(path, reps=30, warmup=20):
     import torch
     from bwd_rmsnorm_fwd_amd import synth
@@ -386,12 +407,7 @@ def suite(path, reps=30, warmup=20):
         out.append(d)
         print(json.dumps(d), file=sys.stderr, flush=True)
 
-    # Rows wider than every configured workload (bf16, 128 MB per tensor):
-    # the forward's 512 x 4 tile at 16384, the backward's register tile there
-    # and its streaming kernel beyond.
-    wide = [synth.Workload(f"wide_bf16_{r}x{h}", synth.BF16, r, h, 1e-6, 701 + k, 711 + k, 721 + k,
-                           731 + k, 741 + k)
-            for k, (r, h) in enumerate(((4096, 16384), (2048, 32768), (1024, 65536)))]
+    wide = [w for w in wide_workloads() if not w.residual]
     plain = [synth.WORKLOADS[n] for n in ("c1_f32_64x896", "c2_bf16_4096x4096",
                                           "c5a_bf16_262144x128", "c5b_bf16_8192x8192")]
     for wl in plain + wide:
@@ -429,8 +445,7 @@ def suite(path, reps=30, warmup=20):
         del sets, C
         torch.cuda.empty_cache()
 
-    wide_res = synth.Workload("wide_bf16_residual_2048x32768", synth.BF16, 2048, 32768, 1e-6,
-                              751, 752, 753, 754, 755, residual=True)
+    wide_res = workload_by_name("wide_bf16_residual_2048x32768")
     for wl in (synth.WORKLOADS["c4_bf16_residual_16384x4096"], wide_res):
         sets = Sets(wl, residual=True, dres=True)
         C = Calls(sets, stream)
@@ -585,7 +600,9 @@ def suite(path, reps=30, warmup=20):
 # ---------------------------------------------------------------- counter passes
 
 COUNTER_WORKLOADS = ["c1_f32_64x896", "c2_bf16_4096x4096", "c5a_bf16_262144x128",
-                     "c5b_bf16_8192x8192", "c4_bf16_residual_16384x4096", "c3_bf16_decode_1x896"]
+                     "c5b_bf16_8192x8192", "c4_bf16_residual_16384x4096",
+                     "wide_bf16_2048x32768", "wide_bf16_1024x65536",
+                     "wide_bf16_residual_2048x32768", "c3_bf16_decode_1x896"]
 
 
 def counters_pass(n):
@@ -601,8 +618,8 @@ def counters_pass(n):
 
     stream = torch.cuda.current_stream()
     for name in COUNTER_WORKLOADS:
-        wl = synth.WORKLOADS[name]
-        residual = name.startswith("c4")
+        wl = workload_by_name(name)
+        residual = wl.residual
         sets = Sets(wl, k=1 if wl.rows == 1 else None, residual=residual, dres=residual)
         C = Calls(sets, stream)
         partials = torch.empty(4, dtype=torch.float32, device="cuda")

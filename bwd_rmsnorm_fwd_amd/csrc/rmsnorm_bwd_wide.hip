@@ -23,7 +23,7 @@ namespace rms {
 // chunks per lane).  Holding such a row in registers across its row sum
 // spills, so a workgroup of WW lanes owns one row at a time and streams it
 // twice in slices of WW * VEC elements: pass A forms the row sums, pass B reads
-// each slice again (from L2 or the Infinity Cache: pass A's loads are
+// each slice again (from L2 where it still holds them: pass A's loads are
 // cached, pass B's are the last use) to form dx and the dw terms.  Only the
 // dw column sums stay in registers (NS x VEC per lane).  The next slice's
 // loads are in flight while the current one is used, also across the pass
@@ -107,6 +107,7 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
     };
 
     const int64_t G = gridDim.x;
+    constexpr bool kRevB = WW == 1024;  // pass B last slice first
     Slice buf[2];
     int set = 0;
     int64_t row = blockIdx.x;
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             if (s + 1 < NS) load_a(row, s + 1, buf[(s + 1) & 1]);
-            else load_b(row, 0, buf[0]);
+            else load_b(row, kRevB ? NS - 1 : 0, buf[0]);
             const Slice& q = buf[s & 1];
             float xv[VEC], dyv[VEC], wc[VEC];
             unpack(q.x, xv);
@@ -143,14 +144,20 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
             r = rsqrt_f64(ss * inv_h + (double)eps);
         }
         const RowK kq = row_k(r, cs, inv_h, true);
-        // Pass B: dx and the dw terms, slice s while slice s + 1 loads
-        // (after the last slice, the next row's first).
+        // Pass B: dx and the dw terms, slice by slice while the next one
+        // loads (after the last, the next row's first, into buffer 0).  The
+        // 1024-lane builds go last slice first, so that the slices pass A read
+        // last are re-read while L2 still holds them: slice s from buffer
+        // (s + 1) & 1.  (Measured at bf16 2048 x 32768 with dres: 113.8 ->
+        // 109.9 us.  In the 512-lane builds, rows of 256 KB, pass A's data is
+        // gone either way, and the reversed order measured 0.6-3% slower.)
         T* const dxr = dx + row * (int64_t)H;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            if (s + 1 < NS) load_b(row, s + 1, buf[(s + 1) & 1]);
+        for (int j = 0; j < NS; ++j) {
+            const int s = kRevB ? NS - 1 - j : j;
+            if (j + 1 < NS) load_b(row, kRevB ? s - 1 : s + 1, buf[kRevB ? s & 1 : (s + 1) & 1]);
             else load_a(row + G, 0, buf[0]);
-            const Slice& q = buf[s & 1];
+            const Slice& q = buf[kRevB ? (s + 1) & 1 : s & 1];
             float xv[VEC], dyv[VEC], wc[VEC], drv[VEC], o[VEC];
             unpack(q.x, xv);
             unpack(q.dy, dyv);
