@@ -6,6 +6,8 @@
 //   dw_j = sum over rows of dy_j x_j r.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 // Streaming (nontemporal) access to the row tensors: dy/x/dres loads and
@@ -75,6 +77,27 @@ __device__ __forceinline__ void dx_chunk(const float (&xv)[VEC], const float (&d
             o[k] = q.rf * t;
             acc[k] += (dyv[k] * xv[k]) * q.rf;
         }
+    }
+}
+
+// Calls go(dres, rstd) with the two compile-time flags of a wide-row
+// backward launch: a residual-stream gradient is added, and the saved rstd is
+// read (else r is recomputed from x).  Fixing the second at compile time
+// matters there: decided at run time, the recompute path's fp64 sums stay
+// live beside the saved-rstd path's registers (the 512-lane streaming build
+// at 65536 spilled 55 VGPRs, none now: bf16 1024 x 65536 row pass 131.4 ->
+// 111.9 us).  The register tiles keep the run-time choice, which measured
+// faster there (bf16 262144 x 128 row pass 34.9 vs 36.9 us).
+template <typename Args, typename F>
+__host__ inline void bwd_variant(const Args& a, F&& go) {
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if (a.dres) {
+        if (a.rstd) go(T_{}, T_{});
+        else go(T_{}, F_{});
+    } else {
+        if (a.rstd) go(F_{}, T_{});
+        else go(F_{}, F_{});
     }
 }
 

@@ -32,7 +32,7 @@ namespace rms {
 // of WW = 1024 lanes up to 4 slices; wider rows use 512 lanes, whose waves
 // have twice the registers for the larger share of dw sums.
 
-template <typename T, int VEC, int WW, int NS, bool DRES>
+template <typename T, int VEC, int WW, int NS, bool DRES, bool RSTD>
 __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
     const T* dy, const T* __restrict__ x, const T* __restrict__ w,
     const float* __restrict__ rstd, const T* dres, T* dx, float* __restrict__ partial,
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
     __shared__ double red[2 * 2 * NWT];
 
     const int lt = threadIdx.x;
-    const bool has_rstd = rstd != nullptr;
+    constexpr bool has_rstd = RSTD;  // saved statistic (else r from x)
     const double inv_h = 1.0 / (double)H;
     const uint32_t row_bytes = (uint32_t)H * (uint32_t)sizeof(T);
     // Slice s of a row is addressed through a resource that starts at the
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(WW) void bwd_rows_wide_kernel(
 // row is read from LDS, every memory operation older than the previous
 // row's dx stores has completed (vmcnt), and the LDS reads have returned
 // (lgkmcnt) before the region is refilled.
-template <typename T, int VEC, bool DRES>
+template <typename T, int VEC, bool DRES, bool RSTD>
 __global__ __launch_bounds__(1024) void bwd_rows_staged_kernel(
     const T* dy, const T* __restrict__ x, const T* __restrict__ w,
     const float* __restrict__ rstd, const T* dres, T* dx, float* __restrict__ partial,
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(1024) void bwd_rows_staged_kernel(
 
     const int lt = threadIdx.x;
     const int wave = lt / kWave;
-    const bool has_rstd = rstd != nullptr;
+    constexpr bool has_rstd = RSTD;  // saved statistic (else r from x)
     const double inv_h = 1.0 / (double)H;
     const uint32_t row_bytes = (uint32_t)H * (uint32_t)sizeof(T);
     uint32_t voff[NCH];
@@ -411,7 +411,7 @@ __device__ __forceinline__ void wait_chunk() {
     asm volatile("" ::: "memory");
 }
 
-template <typename T, int VEC, int WG, int NCH>
+template <typename T, int VEC, int WG, int NCH, bool RSTD>
 __global__ __launch_bounds__(WG) void bwd_rows_ldsrow_kernel(
     const T* dy, const T* __restrict__ x, const T* __restrict__ w,
     const float* __restrict__ rstd, T* dx, float* __restrict__ partial, int64_t rows, int H,
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(WG) void bwd_rows_ldsrow_kernel(
 
     const int lt = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(lt / kWave);
-    const bool has_rstd = rstd != nullptr;
+    constexpr bool has_rstd = RSTD;  // saved statistic (else r from x)
     const double inv_h = 1.0 / (double)H;
     const uint32_t row_bytes = (uint32_t)H * (uint32_t)sizeof(T);
     const uint32_t loff = (uint32_t)lt * VEC * (uint32_t)sizeof(T);  // lane offset in a chunk
@@ -564,15 +564,13 @@ __global__ __launch_bounds__(WG) void bwd_rows_ldsrow_kernel(
 // 115.1; at 4096 x 16384 the 1024 x 2 tile stays (84.5 vs 94.0).
 template <typename T, int VEC, int WW, int NS>
 static hipError_t launch_wide_cfg(const BwdArgs& a, hipStream_t s) {
-    if (a.dres) {
-        hipLaunchKernelGGL((bwd_rows_wide_kernel<T, VEC, WW, NS, true>), dim3(a.G), dim3(WW), 0, s,
+    auto go = [&](auto dres_c, auto rstd_c) {
+        constexpr bool D = decltype(dres_c)::value, RS = decltype(rstd_c)::value;
+        hipLaunchKernelGGL((bwd_rows_wide_kernel<T, VEC, WW, NS, D, RS>), dim3(a.G), dim3(WW), 0, s,
                            (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
                            (const T*)a.dres, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
-    } else {
-        hipLaunchKernelGGL((bwd_rows_wide_kernel<T, VEC, WW, NS, false>), dim3(a.G), dim3(WW), 0, s,
-                           (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
-                           (const T*)nullptr, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
-    }
+    };
+    bwd_variant(a, go);
     return hipGetLastError();
 }
 
@@ -581,9 +579,15 @@ static hipError_t launch_rows_wide(const BwdArgs& a, hipStream_t s) {
     const int64_t n1024 = (a.H + 1024 * VEC - 1) / (1024 * VEC);
     if constexpr (VEC > 1 && RMS_BWD_LDSROW) {
         if (n1024 <= 4 && !a.dres) {
-            hipLaunchKernelGGL((bwd_rows_ldsrow_kernel<T, VEC, 512, 8>), dim3(a.G), dim3(512), 0, s,
-                               (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd, (T*)a.dx,
-                               a.partial, a.rows, a.H, a.ldp, a.eps);
+            if (a.rstd) {
+                hipLaunchKernelGGL((bwd_rows_ldsrow_kernel<T, VEC, 512, 8, true>), dim3(a.G),
+                                   dim3(512), 0, s, (const T*)a.dy, (const T*)a.x, (const T*)a.w,
+                                   a.rstd, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
+            } else {
+                hipLaunchKernelGGL((bwd_rows_ldsrow_kernel<T, VEC, 512, 8, false>), dim3(a.G),
+                                   dim3(512), 0, s, (const T*)a.dy, (const T*)a.x, (const T*)a.w,
+                                   a.rstd, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
+            }
             return hipGetLastError();
         }
     }
@@ -596,15 +600,13 @@ static hipError_t launch_rows_wide(const BwdArgs& a, hipStream_t s) {
 
 template <typename T, int VEC>
 static hipError_t launch_rows_staged(const BwdArgs& a, hipStream_t s) {
-    if (a.dres) {
-        hipLaunchKernelGGL((bwd_rows_staged_kernel<T, VEC, true>), dim3(a.G), dim3(1024), 0, s,
+    auto go = [&](auto dres_c, auto rstd_c) {
+        constexpr bool D = decltype(dres_c)::value, RS = decltype(rstd_c)::value;
+        hipLaunchKernelGGL((bwd_rows_staged_kernel<T, VEC, D, RS>), dim3(a.G), dim3(1024), 0, s,
                            (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd, (const T*)a.dres,
                            (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
-    } else {
-        hipLaunchKernelGGL((bwd_rows_staged_kernel<T, VEC, false>), dim3(a.G), dim3(1024), 0, s,
-                           (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd, (const T*)nullptr,
-                           (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
-    }
+    };
+    bwd_variant(a, go);
     return hipGetLastError();
 }
 
