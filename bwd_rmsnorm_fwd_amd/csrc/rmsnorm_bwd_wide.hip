@@ -285,6 +285,9 @@ __global__ __launch_bounds__(1024) void bwd_rows_staged_kernel(
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         const float rs = rs_next;
         stage_row(row + G, rs_next);
+        // The waits count this row's dx stores after the staging loads: keep
+        // the compiler from moving a store above them.
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             if (!cok[c]) {
@@ -517,6 +520,7 @@ __global__ __launch_bounds__(WG) void bwd_rows_ldsrow_kernel(
         }
         const RowK kq = row_k(r, cs, inv_h, true);
         rs = load_rs(row + G);
+        asm volatile("" ::: "memory");  // rstd's load stays older than the chunks' loads
         // Pass B: dx and the dw terms from the chunks in LDS; each chunk's
         // region is refilled with the next row's chunk once read.
         T* const dxr = dx + row * (int64_t)H;
@@ -525,6 +529,9 @@ __global__ __launch_bounds__(WG) void bwd_rows_ldsrow_kernel(
             Pack<T, VEC> px, pdy;
             read_chunk(cc, px, pdy);
             stage_chunk(row + G, c);
+            // The waits count this chunk's dx store after its two loads: keep
+            // the compiler from moving the store (or anything) above them.
+            asm volatile("" ::: "memory");
             float xv[VEC], dyv[VEC], wc[VEC], drv[VEC], o[VEC];
             unpack(px, xv);
             unpack(pdy, dyv);
