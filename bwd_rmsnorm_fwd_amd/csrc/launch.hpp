@@ -66,7 +66,9 @@ int partial_ld(int64_t H);
 hipError_t launch_fwd(DType dt, int vec, const FwdArgs& a, bool residual, hipStream_t s);
 hipError_t launch_bwd_rows(DType dt, int vec, const BwdArgs& a, hipStream_t s);
 // Rows of 1024-lane teams: with two 16-byte chunks per lane (vec > 1), the
-// LDS-staged kernel; with four or more, the streaming kernel.
+// LDS-staged kernel; with four or more, the row-in-LDS kernel where x and dy
+// of a row fit in LDS and no dres is given (launch_bwd_wide picks it), else
+// the streaming kernel.
 hipError_t launch_bwd_staged(DType dt, int vec, const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_wide(DType dt, int vec, const BwdArgs& a, hipStream_t s);
 hipError_t launch_dw_reduce(DType dt, const float* partial, int G, int ldp, int H, void* dw,

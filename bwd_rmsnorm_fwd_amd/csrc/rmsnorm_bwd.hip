@@ -17,8 +17,9 @@
 //     block's rows; rstd is the forward's saved statistic (or is recomputed
 //     from x when none is given).  Rows of 1024-lane teams with two chunks
 //     per lane stage the next row in LDS instead of registers
-//     (bwd_rows_staged_kernel); wider rows, too large for either, are
-//     streamed twice, one row per workgroup (bwd_rows_wide_kernel).
+//     (bwd_rows_staged_kernel); wider rows are held in LDS one at a time
+//     where x and dy fit (bwd_rows_ldsrow_kernel), else streamed twice, one
+//     row per workgroup (bwd_rows_wide_kernel).
 //   * The row sums c (and sum x^2 when recomputing) are exact fp32 products
 //     (for bf16 inputs) accumulated in fp64, so c and r carry no cancellation
 //     error.  dx uses k = r^2 c split into two floats, k_hi + k_lo, applied

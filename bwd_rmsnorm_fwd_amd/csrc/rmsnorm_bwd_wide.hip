@@ -1,8 +1,9 @@
 // Backward row pass for rows too wide for the register tiles of
 // bwd_rows_kernel, gfx950: an LDS-staged form for 1024-lane teams with two
-// 16-byte chunks per lane, and a streaming form for wider rows.  Both write
-// the same per-workgroup dw partial rows as bwd_rows_kernel, reduced by the
-// same dw reduce pass.
+// 16-byte chunks per lane (the next row staged in LDS), a row-in-LDS form for
+// rows of up to 128 KB of x and dy without a residual-stream gradient, and a
+// streaming form for the rest.  All write the same per-workgroup dw partial
+// rows as bwd_rows_kernel, reduced by the same dw reduce pass.
 //
 // P1 = "训推加速 Qwen3 实战：从“调包”到手写 Triton Kernel（含 backward）":
 //   §5.3 the backward formulas; §5.4 dw in two passes rather than atomics.
