@@ -589,23 +589,27 @@ WIDE_MULTI = [(synth.BF16, 600, 12288), (synth.BF16, 520, 24576), (synth.BF16, 3
               (synth.BF16, 270, 20000), (synth.BF16, 3, 32760), (synth.F32, 260, 16384)]
 
 
-@pytest.mark.parametrize("mode", ["saved_rstd", "recompute", "dres"])
+@pytest.mark.parametrize("mode", ["saved_rstd", "recompute", "dres", "dres_recompute"])
 @pytest.mark.parametrize("dtype,rows,H", WIDE + WIDE_MULTI)
 def test_bwd_wide_rows(dtype, rows, H, mode):
+    """Every wide-row kernel in each of its four builds: with or without a
+    residual-stream gradient, saved or recomputed rstd."""
+    recompute = mode.endswith("recompute")
+    with_dres = mode.startswith("dres")
     wl, x, w, dy, _, dres = _inputs(rows, H, dtype, seed=17 * rows + H, outliers=0.01)
     x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
     _, r64 = oracle.rmsnorm_fwd(x64, w64, wl.eps)
     rstd32 = round_f32(r64)
     xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
-    rstd_d = torch.from_numpy(rstd32.astype(np.float32)).to(DEV) if mode != "recompute" else None
-    dres_d = to_dev(dres, dtype) if mode == "dres" else None
+    rstd_d = None if recompute else torch.from_numpy(rstd32.astype(np.float32)).to(DEV)
+    dres_d = to_dev(dres, dtype) if with_dres else None
     dx = _empty(rows, H, dtype)
     dw = torch.full((H,), float("nan"), dtype=torch_dtype(dtype), device=DEV)
     B.rmsnorm_bwd(dyd, xd, wd, rstd_d, dres_d, dx, dw, _ws(rows, H, dtype), wl.eps)
     torch.cuda.synchronize()
     dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps,
-                                  rstd=None if mode == "recompute" else rstd32,
-                                  dres=synth.to_f64(dres, dtype) if mode == "dres" else None)
+                                  rstd=None if recompute else rstd32,
+                                  dres=synth.to_f64(dres, dtype) if with_dres else None)
     assert_output("dx", f64(dx), dxo, dtype)
     assert_dw(f64(dw), dwo, dtype)
 
