@@ -57,6 +57,34 @@ def build(out_path: str = LIB_PATH, defines=(), build_dir: str | None = None, jo
     return out_path
 
 
+def resource_usage(src: str, defines=()) -> dict:
+    """Per-kernel register, scratch and LDS use of one source file for gfx950,
+    from the compiler's kernel resource-usage remarks (a device-only compile,
+    no object kept).  Returns {mangled kernel name: {field: int}} with the
+    fields TotalSGPRs, VGPRs, AGPRs, ScratchSize, Occupancy, SGPRsSpill,
+    VGPRsSpill, LDSSize."""
+    import re
+    import tempfile
+    dflags = [f"-D{d}" for d in defines]
+    with tempfile.TemporaryDirectory() as td:
+        cmd = [HIPCC, *FLAGS, *dflags, "--cuda-device-only", "-Rpass-analysis=kernel-resource-usage",
+               "-c", os.path.join(CSRC, src), "-o", os.path.join(td, "k.o")]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    out: dict = {}
+    cur = None
+    for line in r.stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+) \[-Rpass", line)
+        if m and cur is not None:
+            cur[m.group(1).replace(" ", "")] = int(m.group(2))
+    return out
+
+
 BENCH_LOOPS_SRC = os.path.join(PKG, "bench_loops.cpp")
 BENCH_LOOPS_PATH = os.path.join(PKG, "libbench_loops.so")
 

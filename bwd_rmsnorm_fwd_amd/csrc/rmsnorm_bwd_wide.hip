@@ -602,7 +602,12 @@ static hipError_t launch_rows_wide(const BwdArgs& a, hipStream_t s) {
     if (n1024 <= 4) return launch_wide_cfg<T, VEC, 1024, 4>(a, s);
     const int64_t n512 = (a.H + 512 * VEC - 1) / (512 * VEC);
     if (n512 <= 16) return launch_wide_cfg<T, VEC, 512, 16>(a, s);
-    if (n512 <= 32) return launch_wide_cfg<T, VEC, 512, 32>(a, s);
+    // 32 slices of 512 x VEC only where RMSNORM_MAX_H (65536) needs them: not
+    // for bf16 with 128-bit access (16 slices reach 65536), so that build is
+    // not instantiated.
+    if constexpr (512 * 16 * VEC < 65536) {
+        if (n512 <= 32) return launch_wide_cfg<T, VEC, 512, 32>(a, s);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -229,7 +229,10 @@ static hipError_t dispatch(const FwdArgs& a, bool residual, hipStream_t s) {
     RMS_CASE(1, 1) RMS_CASE(2, 1) RMS_CASE(4, 1) RMS_CASE(8, 1) RMS_CASE(16, 1) RMS_CASE(32, 1)
     RMS_CASE(64, 1) RMS_CASE(64, 2) RMS_CASE(128, 2) RMS_CASE(256, 2) RMS_CASE(512, 1)
     RMS_CASE(512, 2) RMS_CASE(512, 4)
-    RMS_CASE(1024, 2) RMS_CASE(1024, 4) RMS_CASE(1024, 8) RMS_CASE(1024, 16)
+    RMS_CASE(1024, 2) RMS_CASE(1024, 4) RMS_CASE(1024, 8)
+    // 1024 x 16 only where the widest row (65536) needs it: not for bf16 with
+    // 128-bit access, whose 1024 x 8 tile already covers 65536.
+    if constexpr (1024 * 8 * VEC < 65536) { RMS_CASE(1024, 16) }
 #undef RMS_CASE
     return hipErrorInvalidValue;
 }

@@ -87,3 +87,22 @@ def assert_rstd(g: np.ndarray, o: np.ndarray):
 
 def round_f32(a: np.ndarray) -> np.ndarray:
     return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def oracle_stat(ro: np.ndarray):
+    """The stored statistic taken from the oracle: the fp32 rounding of the
+    oracle's double r (as float64 values for the oracle, and as a device fp32
+    tensor for the library), so that both backwards get the same input and
+    no expected value depends on a number the GPU produced."""
+    r32 = round_f32(ro)
+    return r32, torch.from_numpy(r32.astype(np.float32)).to(DEV)
+
+
+def assert_rstd_rounded(g: np.ndarray, ro: np.ndarray):
+    """The GPU forward's rstd must be the fp32 rounding of the oracle's r on
+    every row (the row sums are exact products accumulated in fp64, so r is
+    known to far more than fp32 precision on both sides)."""
+    r32 = round_f32(ro)
+    bad = np.flatnonzero(g != r32)
+    assert bad.size == 0, (f"rstd differs from fp32(oracle r) on {bad.size} rows, first "
+                           f"{bad[:5].tolist()}: {g[bad[:5]].tolist()} vs {r32[bad[:5]].tolist()}")

@@ -1,6 +1,12 @@
 """C ABI checks that need no GPU: the library loads, exports every function
 include/*.h declares, and rejects bad arguments before touching the device.
-Only validation paths are called here (no kernel is launched)."""
+
+The validation checks pass pseudo-pointers that must be rejected before any
+launch.  So that a change in the order of the checks could never launch a
+kernel on an unmapped address, each of them runs in a child process that
+sees no GPU (HIP_VISIBLE_DEVICES and ROCR_VISIBLE_DEVICES name no device):
+there a launch that slipped through returns an error instead of running.
+The child first confirms that HIP reports no device, else it refuses to run."""
 import ctypes
 import glob
 import os
@@ -63,7 +69,7 @@ def _fwd(*a):
 MIS = ctypes.c_void_p(0x1001)  # misaligned pseudo-pointer: rejected before any launch
 
 
-def test_fwd_validation():
+def _check_fwd_validation():
     nul = None
     stream = None
     assert _fwd(nul, nul, nul, nul, 4, 64, 1e-6, B.BF16, stream) == B.EINVAL       # null pointers
@@ -78,7 +84,7 @@ def test_fwd_validation():
     assert _fwd(MIS, MIS, MIS, nul, 0, 64, 1e-6, B.BF16, stream) == B.OK           # rows = 0: no-op
 
 
-def test_bwd_validation_and_workspace():
+def _check_bwd_validation_and_workspace():
     L = B.lib()
     need = L.rmsnorm_bwd_workspace_bytes(4096, 4096, B.BF16)
     assert need > 0 and need % 16 == 0
@@ -104,7 +110,7 @@ def test_bwd_validation_and_workspace():
     assert sizes == sorted(sizes) and sizes[-1] == sizes[-2]
 
 
-def test_splitrow_validation():
+def _check_splitrow_validation():
     L = B.lib()
     A = ctypes.c_void_p(0x10000)
     assert L.rmsnorm_splitrow_partials_count(1, 4) == 4
@@ -119,7 +125,7 @@ def test_splitrow_validation():
     assert f(A, A, A, None, A, 4, 0, 896, 1e-6, 4, B.BF16, None) == B.EINVAL        # rows = 0
 
 
-def test_gemv_validation():
+def _check_gemv_validation():
     L = B.lib()
     A = ctypes.c_void_p(0x10000)
     assert L.decode_gemv_partials_count(1024, 4) == 4096
@@ -133,6 +139,33 @@ def test_gemv_validation():
     assert f(A, None, A, None, 0, 1024, 896, 1, B.BF16, None) == B.EINVAL     # x missing
     assert f(A, A, A, None, 0, 0, 896, 1, B.BF16, None) == B.EINVAL           # N = 0
     assert f(MIS, A, A, None, 0, 8, 896, 1, B.BF16, None) == B.EALIGN
+
+
+HIDDEN_ENV = {"HIP_VISIBLE_DEVICES": "-1", "ROCR_VISIBLE_DEVICES": "-1", "CUDA_VISIBLE_DEVICES": "-1"}
+
+CHILD = r"""
+import ctypes, os, sys
+sys.path.insert(0, {tests!r}); sys.path.insert(0, {root!r})
+hip = ctypes.CDLL("libamdhip64.so")
+n = ctypes.c_int(-1)
+st = hip.hipGetDeviceCount(ctypes.byref(n))
+if st == 0 and n.value > 0:
+    print("a GPU is visible to the validation child", file=sys.stderr)
+    sys.exit(3)
+import test_abi_host as t
+getattr(t, {fn!r})()
+print("ok")
+"""
+
+
+@pytest.mark.parametrize("check", ["_check_fwd_validation", "_check_bwd_validation_and_workspace",
+                                   "_check_splitrow_validation", "_check_gemv_validation"])
+def test_validation_without_a_device(check):
+    env = dict(os.environ, **HIDDEN_ENV)
+    code = CHILD.format(tests=os.path.dirname(os.path.abspath(__file__)), root=ROOT, fn=check)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), (r.returncode, r.stdout, r.stderr)
 
 
 def test_binding_rejects_mismatched_tensors():

@@ -15,8 +15,8 @@ import torch
 import oracle
 from bwd_rmsnorm_fwd_amd import binding as B
 from bwd_rmsnorm_fwd_amd import synth
-from _gpu_util import (DEV, assert_dw, assert_output, assert_rstd, f64, round_f32, to_dev,
-                       torch_dtype)
+from _gpu_util import (DEV, assert_dw, assert_output, assert_rstd, assert_rstd_rounded, f64,
+                       oracle_stat, to_dev, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +31,11 @@ def _ws(rows, H, dtype):
 
 @pytest.mark.parametrize("name", TRAIN)
 def test_workload_fwd_bwd(name):
+    """Forward, then the backward three ways: given the oracle's statistic
+    (fp32 rounding of its double r, the same input on both sides), chained
+    from the GPU forward's saved rstd (which must equal that statistic on
+    every row, so the chained dx and dw must equal the first ones bitwise),
+    and recomputing r from x (the oracle recomputes it in double)."""
     wl = synth.WORKLOADS[name]
     rows, H, dt = wl.rows, wl.H, wl.dtype
     print(f"[full] {name}: rows={rows} H={H} dtype={dt}", flush=True)
@@ -39,32 +44,48 @@ def test_workload_fwd_bwd(name):
     td = torch_dtype(dt)
     y = torch.empty((rows, H), dtype=td, device=DEV)
     rstd = torch.empty(rows, device=DEV)
-    dx = torch.empty((rows, H), dtype=td, device=DEV)
-    dw = torch.empty(H, dtype=td, device=DEV)
-    ws = _ws(rows, H, dt)
     B.rmsnorm_fwd(xd, wd, y, rstd, wl.eps)
-    B.rmsnorm_bwd_rows(dyd, xd, wd, rstd, None, dx, ws, wl.eps)
-    B.rmsnorm_bwd_dw_reduce(ws, dw, rows)
     torch.cuda.synchronize()
     x64, w64, dy64 = (synth.to_f64(a, dt) for a in (x, w, dy))
     del x, dy
     yo, ro = oracle.rmsnorm_fwd(x64, w64, wl.eps)
     e_y = assert_output("y", f64(y), yo, dt)
-    del yo
+    del yo, y
     e_r = assert_rstd(f64(rstd), ro)
-    rs = f64(rstd)
-    # Backward against the oracle given the same stored fp32 statistic; the
-    # statistic itself is the fp32 rounding of the oracle's r.
-    n_tie = int(np.sum(rs != round_f32(ro)))
-    assert n_tie <= max(1, rows // 100000), f"{n_tie} rows with rstd != rounded r"
-    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=rs)
+    assert_rstd_rounded(f64(rstd), ro)
+    r32, r32_d = oracle_stat(ro)
+
+    def bwd(stat):
+        dx = torch.empty((rows, H), dtype=td, device=DEV)
+        dw = torch.empty(H, dtype=td, device=DEV)
+        ws = _ws(rows, H, dt)
+        B.rmsnorm_bwd_rows(dyd, xd, wd, stat, None, dx, ws, wl.eps)
+        B.rmsnorm_bwd_dw_reduce(ws, dw, rows)
+        torch.cuda.synchronize()
+        return dx, dw
+
+    dx, dw = bwd(r32_d)
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=r32)
     e_dx = assert_output("dx", f64(dx), dxo, dt)
     e_dw = assert_dw(f64(dw), dwo, dt)
+    del dxo
+    dxc, dwc = bwd(rstd)
+    assert torch.equal(dxc.view(torch.int16 if dt == synth.BF16 else torch.int32),
+                       dx.view(torch.int16 if dt == synth.BF16 else torch.int32)), "chained dx"
+    assert torch.equal(dwc, dw), "chained dw"
+    del dxc, dwc, dx, dw
+    dxq, dwq = bwd(None)
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=None)
+    e_dxq = assert_output("dx (recompute)", f64(dxq), dxo, dt)
+    e_dwq = assert_dw(f64(dwq), dwo, dt)
     print(f"[full] {name}: y {e_y:.3g}  rstd {e_r:.3g}  dx {e_dx:.3g}  dw {e_dw:.3g}  "
-          f"rstd!=round(r): {n_tie}", flush=True)
+          f"recompute: dx {e_dxq:.3g}  dw {e_dwq:.3g}", flush=True)
 
 
 def test_workload_residual_fwd_bwd():
+    """Residual forward, then its backward with dres given the oracle's
+    statistic, chained from the GPU forward's rstd (bitwise the same), and
+    recomputing r from h."""
     wl = synth.WORKLOADS["c4_bf16_residual_16384x4096"]
     rows, H, dt = wl.rows, wl.H, wl.dtype
     print(f"[full] {wl.name}: rows={rows} H={H}", flush=True)
@@ -74,10 +95,7 @@ def test_workload_residual_fwd_bwd():
     h = torch.empty((rows, H), dtype=td, device=DEV)
     y = torch.empty((rows, H), dtype=td, device=DEV)
     rstd = torch.empty(rows, device=DEV)
-    dh = torch.empty((rows, H), dtype=td, device=DEV)
-    dw = torch.empty(H, dtype=td, device=DEV)
     B.rmsnorm_residual_fwd(xd, rd, wd, h, y, rstd, wl.eps)
-    B.rmsnorm_bwd(dyd, h, wd, rstd, drd, dh, dw, _ws(rows, H, dt), wl.eps)
     torch.cuda.synchronize()
     del xd, rd
     ho, yo, ro = oracle.rmsnorm_residual_fwd(synth.to_f64(x, dt), synth.to_f64(res, dt),
@@ -85,14 +103,34 @@ def test_workload_residual_fwd_bwd():
     del x, res
     assert np.array_equal(f64(h), ho), "h must be bit-exact"
     e_y = assert_output("y", f64(y), yo, dt)
-    del yo
+    del yo, y
     e_r = assert_rstd(f64(rstd), ro)
-    dho, dwo = oracle.rmsnorm_bwd(synth.to_f64(dy, dt), ho, synth.to_f64(w, dt), wl.eps,
-                                  rstd=f64(rstd), dres=synth.to_f64(dres, dt))
+    assert_rstd_rounded(f64(rstd), ro)
+    r32, r32_d = oracle_stat(ro)
+    dy64, w64, dres64 = synth.to_f64(dy, dt), synth.to_f64(w, dt), synth.to_f64(dres, dt)
+
+    def bwd(stat):
+        dh = torch.empty((rows, H), dtype=td, device=DEV)
+        dw = torch.empty(H, dtype=td, device=DEV)
+        B.rmsnorm_bwd(dyd, h, wd, stat, drd, dh, dw, _ws(rows, H, dt), wl.eps)
+        torch.cuda.synchronize()
+        return dh, dw
+
+    dh, dw = bwd(r32_d)
+    dho, dwo = oracle.rmsnorm_bwd(dy64, ho, w64, wl.eps, rstd=r32, dres=dres64)
     e_dh = assert_output("dh", f64(dh), dho, dt)
     e_dw = assert_dw(f64(dw), dwo, dt)
-    print(f"[full] {wl.name}: y {e_y:.3g}  rstd {e_r:.3g}  dh {e_dh:.3g}  dw {e_dw:.3g}",
-          flush=True)
+    del dho
+    dhc, dwc = bwd(rstd)
+    assert torch.equal(dhc.view(torch.int16), dh.view(torch.int16)), "chained dh"
+    assert torch.equal(dwc.view(torch.int16), dw.view(torch.int16)), "chained dw"
+    del dhc, dwc, dh, dw
+    dhq, dwq = bwd(None)
+    dho, dwo = oracle.rmsnorm_bwd(dy64, ho, w64, wl.eps, rstd=None, dres=dres64)
+    e_dhq = assert_output("dh (recompute)", f64(dhq), dho, dt)
+    e_dwq = assert_dw(f64(dwq), dwo, dt)
+    print(f"[full] {wl.name}: y {e_y:.3g}  rstd {e_r:.3g}  dh {e_dh:.3g}  dw {e_dw:.3g}  "
+          f"recompute: dh {e_dhq:.3g}  dw {e_dwq:.3g}", flush=True)
 
 
 @pytest.mark.parametrize("splits", [1, 4, 8, 16])
@@ -142,13 +180,16 @@ def test_beyond_2_31_elements(P, H):
     def tile(t):
         return t.repeat(reps, 1)[:rows].contiguous()
 
-    def run(xd, dyd, rd, n):
+    def run(xd, dyd, rd, n, stat=None):
+        """Forward, backward (given `stat`, else chained from this forward's
+        rstd) and residual forward on n rows."""
         y = torch.empty((n, H), dtype=torch.bfloat16, device=DEV)
         rstd = torch.empty(n, device=DEV)
         dx = torch.empty((n, H), dtype=torch.bfloat16, device=DEV)
         dw = torch.empty(H, dtype=torch.bfloat16, device=DEV)
         B.rmsnorm_fwd(xd, ws_, y, rstd, wl.eps)
-        B.rmsnorm_bwd(dyd, xd, ws_, rstd, None, dx, dw, _ws(n, H, dt), wl.eps)
+        B.rmsnorm_bwd(dyd, xd, ws_, rstd if stat is None else stat, None, dx, dw, _ws(n, H, dt),
+                      wl.eps)
         h = torch.empty((n, H), dtype=torch.bfloat16, device=DEV)
         yr = torch.empty((n, H), dtype=torch.bfloat16, device=DEV)
         rr = torch.empty(n, device=DEV)
@@ -156,17 +197,22 @@ def test_beyond_2_31_elements(P, H):
         torch.cuda.synchronize()
         return y, rstd, dx, dw, h, yr, rr
 
-    small = run(xs, dys, rs_, P)
+    # The block: its backward takes the oracle's statistic (fp32 of its r),
+    # which the block's forward must reproduce bitwise.
     x64, w64, dy64 = (synth.to_f64(a, dt) for a in (x, w, dy))
     yo, ro = oracle.rmsnorm_fwd(x64, w64, wl.eps)
+    r32, r32_d = oracle_stat(ro)
+    small = run(xs, dys, rs_, P, stat=r32_d)
     assert_output("y", f64(small[0]), yo, dt)
     assert_rstd(f64(small[1]), ro)
-    rs = f64(small[1])
-    dxo, _ = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=rs)
+    assert_rstd_rounded(f64(small[1]), ro)
+    dxo, _ = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=r32)
     assert_output("dx", f64(small[2]), dxo, dt)
     ho, _, _ = oracle.rmsnorm_residual_fwd(x64, synth.to_f64(res, dt), w64, wl.eps, oracle.H_BF16)
     assert np.array_equal(f64(small[4]), ho), "h must be bit-exact"
 
+    # The large run chains its own forward's rstd into its backward; its rows
+    # must equal the block's (whose rstd is the oracle's statistic) bitwise.
     xb, dyb, rb = tile(xs), tile(dys), tile(rs_)
     assert xb.numel() > (1 << 31)
     big = run(xb, dyb, rb, rows)
@@ -180,6 +226,6 @@ def test_beyond_2_31_elements(P, H):
         assert torch.equal(b[full:], s[:rows - full]), f"{name}: tail rows differ from the block"
     count = np.full(P, rows // P, dtype=np.float64)
     count[:rows - full] += 1
-    _, dwo = oracle.rmsnorm_bwd(dy64 * count[:, None], x64, w64, wl.eps, rstd=rs)
+    _, dwo = oracle.rmsnorm_bwd(dy64 * count[:, None], x64, w64, wl.eps, rstd=r32)
     e_dw = assert_dw(f64(big[3]), dwo, dt)
     print(f"[full] beyond 2^31 elements: rows match the block bitwise, dw {e_dw:.3g}", flush=True)

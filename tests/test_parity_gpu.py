@@ -18,8 +18,8 @@ import torch
 import oracle
 from bwd_rmsnorm_fwd_amd import binding as B
 from bwd_rmsnorm_fwd_amd import synth
-from _gpu_util import (DEV, assert_dw, assert_output, assert_rstd, f64, round_f32, to_dev,
-                       torch_dtype)
+from _gpu_util import (DEV, assert_dw, assert_output, assert_rstd, assert_rstd_rounded, f64,
+                       oracle_stat, round_f32, to_dev, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -221,15 +221,17 @@ def test_degenerate_rows(dtype, H):
     y, rstd = _empty(rows, H, dtype), torch.full((rows,), float("nan"), device=DEV)
     dx = _empty(rows, H, dtype)
     dw = torch.full((H,), float("nan"), dtype=torch_dtype(dtype), device=DEV)
-    B.rmsnorm_fwd(xd, wd, y, rstd, eps)
-    B.rmsnorm_bwd(dyd, xd, wd, rstd, None, dx, dw, _ws(rows, H, dtype), eps)
-    torch.cuda.synchronize()
     yo, ro = oracle.rmsnorm_fwd(x64, w64, eps)
+    r32, r32_d = oracle_stat(ro)
+    B.rmsnorm_fwd(xd, wd, y, rstd, eps)
+    B.rmsnorm_bwd(dyd, xd, wd, r32_d, None, dx, dw, _ws(rows, H, dtype), eps)
+    torch.cuda.synchronize()
     assert_output("y", f64(y), yo, dtype)
     assert_rstd(f64(rstd), ro)
+    assert_rstd_rounded(f64(rstd), ro)
     assert np.all(f64(y)[0] == 0.0), "a zero row gives y = 0"
     assert f64(rstd)[0] == float(np.float32(1.0 / math.sqrt(eps))), "zero row: r = 1/sqrt(eps)"
-    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, eps, rstd=f64(rstd))
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, eps, rstd=r32)
     assert_output("dx", f64(dx), dxo, dtype)
     assert_dw(f64(dw), dwo, dtype)
 
@@ -294,6 +296,9 @@ def test_random_shapes(k):
     torch.cuda.synchronize()
     assert_output("y", f64(y), yo, dtype)
     assert_rstd(f64(rstd), ro)
+    # The GPU backward chains the forward's rstd, which must be the oracle's
+    # statistic bitwise; the oracle is given that statistic from its own r.
+    assert_rstd_rounded(f64(rstd), ro)
     dres_d = to_dev(dres, dtype) if mode == "dres" else None
     dx = _empty(rows, H, dtype)
     dw = torch.full((H,), float("nan"), dtype=torch_dtype(dtype), device=DEV)
@@ -301,7 +306,7 @@ def test_random_shapes(k):
                   _ws(rows, H, dtype), wl.eps)
     torch.cuda.synchronize()
     dxo, dwo = oracle.rmsnorm_bwd(dy64, xin64, w64, wl.eps,
-                                  rstd=None if mode == "recompute" else f64(rstd),
+                                  rstd=None if mode == "recompute" else round_f32(ro),
                                   dres=synth.to_f64(dres, dtype) if mode == "dres" else None)
     assert_output("dx", f64(dx), dxo, dtype)
     assert_dw(f64(dw), dwo, dtype)
@@ -323,12 +328,12 @@ def test_chain_fwd_then_bwd(rows, H, dtype):
     torch.cuda.synchronize()
     yo, ro = oracle.rmsnorm_fwd(x64, w64, wl.eps)
     assert_rstd(f64(rstd), ro)
-    # The GPU's rstd is the correctly rounded fp32 r except on rare exact ties;
-    # the backward with it matches the oracle given that same fp32 value.
-    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=f64(rstd))
+    # The GPU's rstd must be the fp32 rounding of the oracle's r on every row;
+    # the chained backward then matches the oracle given that statistic.
+    assert_rstd_rounded(f64(rstd), ro)
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=round_f32(ro))
     assert_output("dx", f64(dx), dxo, dtype)
     assert_dw(f64(dw), dwo, dtype)
-    assert np.array_equal(f64(rstd), round_f32(ro)), "rstd is not the rounded double r"
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -377,7 +382,8 @@ def test_unaligned_pointers_use_scalar_path(dtype):
     x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
     yo, ro = oracle.rmsnorm_fwd(x64, w64, wl.eps)
     assert_output("y", f64(y), yo, dtype)
-    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=f64(rstd))
+    assert_rstd_rounded(f64(rstd), ro)
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, wl.eps, rstd=round_f32(ro))
     assert_output("dx", f64(dx), dxo, dtype)
     assert_dw(f64(dw), dwo, dtype)
     assert torch.isnan(ybuf[0]) and torch.isnan(dxbuf[0])
@@ -503,7 +509,7 @@ def test_graph_capture_replays_match_eager(rows, H):
     """Every entry point records into a HIP graph (no allocation, no sync, no
     memset inside); replays, with eager work and synchronisation in between,
     reproduce the eager results bit for bit (one row block per backward
-    workgroup, and three to four)."""
+    workgroup, and three to four), and the replayed outputs match the oracle."""
     dtype = synth.BF16
     wl, x, w, dy, res, dres = _inputs(rows, H, dtype, seed=77)
     xd, wd, dyd, rd, drd = (to_dev(a, dtype) for a in (x, w, dy, res, dres))
@@ -543,6 +549,19 @@ def test_graph_capture_replays_match_eager(rows, H):
             assert torch.equal(out[k].view(torch.int16), ref[k].view(torch.int16)), (rep, k)
         assert torch.equal(dw.view(torch.int16), ref_dw.view(torch.int16))
         assert torch.equal(rstd, ref_r)
+    # The last replay's outputs against the oracle (not only against eager).
+    x64, w64, dy64, r64, dr64 = (synth.to_f64(a, dtype) for a in (x, w, dy, res, dres))
+    yo, ro = oracle.rmsnorm_fwd(x64, w64, wl.eps)
+    assert_output("y (replay)", f64(out["y"]), yo, dtype)
+    assert_rstd_rounded(f64(rstd), ro)
+    assert_output("y splitrow (replay)", f64(out["ys"]), yo, dtype)
+    ho, yo2, ro2 = oracle.rmsnorm_residual_fwd(x64, r64, w64, wl.eps, oracle.H_BF16)
+    assert np.array_equal(f64(out["h"]), ho), "h (replay) must be bit-exact"
+    assert_output("y residual (replay)", f64(out["y2"]), yo2, dtype)
+    assert_rstd_rounded(f64(rstd2), ro2)
+    dho, dwo = oracle.rmsnorm_bwd(dy64, ho, w64, wl.eps, rstd=round_f32(ro2), dres=dr64)
+    assert_output("dh (replay)", f64(out["dx"]), dho, dtype)
+    assert_dw(f64(dw), dwo, dtype)
 
 
 @pytest.mark.parametrize("dtype,rows,H", [(synth.BF16, 3, 32768), (synth.BF16, 2, 65536),
@@ -564,8 +583,9 @@ def test_widest_rows(dtype, rows, H):
     assert np.array_equal(f64(h), ho)
     assert_output("y", f64(y), yo, dtype)
     assert_rstd(f64(rstd), ro)
+    assert_rstd_rounded(f64(rstd), ro)
     dxo, dwo = oracle.rmsnorm_bwd(synth.to_f64(dy, dtype), ho, synth.to_f64(w, dtype), wl.eps,
-                                  rstd=f64(rstd), dres=synth.to_f64(dres, dtype))
+                                  rstd=round_f32(ro), dres=synth.to_f64(dres, dtype))
     assert_output("dx", f64(dx), dxo, dtype)
     assert_dw(f64(dw), dwo, dtype)
 

@@ -3,9 +3,10 @@ library's own results (no oracle), up to the full bf16 4096 x 4096 workload in
 the launch configuration the benchmark times.
 
 Scaling by a power of two is exact in binary floating point, so wherever the
-algebra of RMSNorm (Zhang & Sennrich, "Root Mean Square Layer Normalization",
-Eq. 4; the backward of the fused-kernel write-up, "Backward pass" section)
-makes an output scale-equivariant, the kernels must reproduce it bit for bit:
+algebra of RMSNorm makes an output scale-equivariant, the kernels must
+reproduce it bit for bit.  The algebra is that of "训推加速 Qwen3 实战：从
+“调包”到手写 Triton Kernel（含 backward）": §4.1 (the forward,
+y = w x / sqrt(mean(x^2) + eps)) and §5.3 (the backward, dx and dw):
 
   * eps = 0, x -> 4^k x:  y unchanged, rstd -> rstd / 4^k, dx -> dx / 4^k,
     dw unchanged (sum of squares scales by 16^k, its square root by 4^k);
