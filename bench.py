@@ -1,21 +1,27 @@
 #!/usr/bin/env python3
 """RMSNorm forward + backward throughput on one MI355X.
 
-A step is one pass of the hot path over one batch: forward (y, rstd) then the
-backward (dx and the dw partials, then the dw reduce pass) of the bf16
-4096 x 4096 workload (rows = B*T = 4096, H = 4096, outlier feature columns),
-through the library's C ABI.  Inputs are resident in HBM before timing.
-Buffer sets rotate so that consecutive steps touch >= 1 GiB of distinct
-memory, which keeps every step's inputs out of the 256 MB Infinity Cache.
+A step is one pass of the hot path over one batch: the fused residual-add +
+RMSNorm forward (h and y written, rstd saved) then its backward (dh = dx +
+dres and the dw partials, then the dw reduce pass) of the bf16 residual
+workload rows = B*T = 4*4096 = 16384, H = 4096 (the largest configuration,
+the shape of the pages' own forward benchmark), through the library's C ABI.
+Inputs are resident in HBM before timing; buffer sets rotate so that each
+kernel's inputs are out of the 256 MB Infinity Cache.
 
 Prints one JSON line.  `value` is achieved HBM GB/s over the whole step,
-counting the algorithmic bytes only (fwd: x, w read, y, rstd written; bwd: dy,
-x, w, rstd read, dx, dw written).  `roofline` is for the dominant kernel (the
-backward row pass), timed with HIP events on the stream it runs on.
-`cpu_baseline` times the double-precision oracle on the host.
+counting the algorithmic bytes only (residual fwd: x, res, w read, h, y,
+rstd written; bwd: dy, dres, h, w, rstd read, dh, dw written), by wall clock
+over the timed steps.  `roofline` is for the step's dominant kernel, timed
+with HIP events around each of its launches inside the steps, on the stream
+it runs on; its name comes from the library's dry-run report.  `configs`
+gives fwd and bwd µs / GB/s / % of 8 TB/s for every other configuration and
+µs per call for decode (plain, C loop, HIP graph) and the split-K q_proj.
+`cpu_baseline` times the double-precision oracle on the host, on one thread
+and on all the cores this process may use.
 
---suite FILE also measures every workload (fwd, bwd, residual, narrow, wide,
-decode split-row) and writes one JSON object per measurement to FILE.
+--suite FILE also measures every workload in detail (median and P95, wide
+rows, warm cache) and writes one JSON object per measurement to FILE.
 """
 from __future__ import annotations
 
@@ -225,107 +231,319 @@ def step_plan(C, sets, residual=False):
     return plan
 
 
-def bench_step(steps, warmup):
-    """The headline step on the bf16 4096 x 4096 workload.
+HEADLINE = "c4_bf16_residual_16384x4096"
 
-    Region 1 times `steps` steps (forward, backward row pass, dw reduce) back
-    to back, bracketed by synchronisation, with nothing else enqueued between
-    the launches; each step's backward works on a different buffer set than its
-    forward (see step_plan), so both read their inputs from HBM.  Region 2 times each kernel on its own: `steps` launches back
-    to back over the same rotating buffers, bracketed by HIP events recorded
+
+def kernel_names(C, calls):
+    """Names of the kernels each call launches, from the library's dry run
+    (the same entry point and arguments, nothing launched)."""
+    from bwd_rmsnorm_fwd_amd import binding as B
+    out = []
+    for fn, args in calls:
+        lines = B.launches_of(fn, *args)
+        out.append([l.split(" grid=")[0] for l in lines])
+    return out
+
+
+def bench_step(steps, warmup, burst_min=200):
+    """The headline step on the bf16 residual 16384 x 4096 workload.
+
+    First each kernel of the step alone: max(steps, burst_min) back-to-back
+    launches over the rotating buffer sets, bracketed by HIP events recorded
     on the stream the kernels run on; the average per launch is the kernel's
-    duration plus the small dispatch gap between launches."""
+    duration plus the small dispatch gap between launches (this also brings
+    the GPU to its working clocks before the timed steps).  Then `warmup`
+    untimed steps and `steps` timed steps (residual forward, backward row
+    pass with the residual-stream gradient, dw reduce) back to back,
+    bracketed by synchronisation, with nothing else enqueued between the
+    launches; each step's backward works on a different buffer set than its
+    forward (see step_plan), so both read their inputs from HBM."""
     import torch
     from bwd_rmsnorm_fwd_amd import synth
 
-    wl = synth.WORKLOADS["c2_bf16_4096x4096"]
-    sets = Sets(wl)
+    wl = synth.WORKLOADS[HEADLINE]
+    sets = Sets(wl, residual=True, dres=True)
     stream = torch.cuda.current_stream()
     C = Calls(sets, stream)
-    plan = step_plan(C, sets)
+    plan = step_plan(C, sets, residual=True)
+    names = kernel_names(C, plan[0])
 
-    for i in range(max(warmup, sets.k)):
-        f, b, r = plan[i % sets.k]
-        run(f); run(b); run(r)
+    # Each kernel alone, event-bracketed bursts.
+    nb = max(steps, burst_min)
+
+    def burst(idx):
+        for i in range(sets.k):
+            run(plan[i][idx])
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(nb):
+            run(plan[i % sets.k][idx])
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / nb
+
+    per_kernel = [burst(j) for j in range(len(plan[0]))]
+
+    for i in range(warmup):
+        for c in plan[i % sets.k]:
+            run(c)
     torch.cuda.synchronize()
 
-    # Region 1: the step.
+    # The timed steps, wall clock.
     e_start = torch.cuda.Event(enable_timing=True)
     e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e_start.record(stream)
     for i in range(steps):
-        f, b, r = plan[i % sets.k]
-        run(f)
-        run(b)
-        run(r)
+        for c in plan[i % sets.k]:
+            run(c)
     e_end.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
     span_ms = e_start.elapsed_time(e_end) / steps
-
-    # Region 2: each kernel alone, event-bracketed bursts.
-    def burst(idx):
-        for i in range(min(warmup, sets.k)):
-            run(plan[i % sets.k][idx])
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for i in range(steps):
-            run(plan[i % sets.k][idx])
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / steps
-
-    fwd_us, rows_us, red_us = burst(0), burst(1), burst(2)
     e = sets.e
     return {
-        "wl": wl, "k": sets.k, "ms_step": ms_step, "span_ms": span_ms,
-        "fwd_us": fwd_us, "rows_us": rows_us, "reduce_us": red_us,
-        "fwd_bytes": fwd_bytes(wl.rows, wl.H, e), "bwd_bytes": bwd_bytes(wl.rows, wl.H, e),
-        "rows_bytes": bwd_rows_bytes(wl.rows, wl.H, e),
+        "wl": wl, "k": sets.k, "ms_step": ms_step, "span_ms": span_ms, "names": names,
+        "burst": nb,
+        "fwd_us": per_kernel[0], "rows_us": per_kernel[1], "reduce_us": per_kernel[2],
+        "fwd_bytes": fwd_bytes(wl.rows, wl.H, e, residual=True),
+        "bwd_bytes": bwd_bytes(wl.rows, wl.H, e, dres=True),
+        "rows_bytes": bwd_rows_bytes(wl.rows, wl.H, e, dres=True),
     }
 
 
-def cpu_baseline(min_seconds=10.0):
-    """The oracle (plain C, double, one thread) on the same workload."""
+def _pct(nbytes, us):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return round(gbs, 1), round(100 * gbs / PEAK_GBS, 2)
+
+
+def config_table(reps=10, burst=16):
+    """fwd / bwd µs per call (median of `reps` bursts of `burst` back-to-back
+    launches on cold rotating buffers, events at the burst ends), GB/s and %
+    of 8 TB/s over the algorithmic bytes, for every configuration; decode as
+    µs per call over 10,000 back-to-back calls (Python loop, C loop, HIP
+    graph replay); the split-K q_proj likewise."""
+    import numpy as np
+    import torch
+    from bwd_rmsnorm_fwd_amd import binding as B
+    from bwd_rmsnorm_fwd_amd import synth
+
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in ("c1_f32_64x896", "c2_bf16_4096x4096", "c5a_bf16_262144x128",
+                 "c5b_bf16_8192x8192", HEADLINE):
+        wl = synth.WORKLOADS[name]
+        res = wl.residual
+        sets = Sets(wl, residual=res, dres=res)
+        C = Calls(sets, stream)
+        e = sets.e
+        if res:
+            f_calls = [(C.residual_fwd(s),) for s in sets.sets]
+            b_calls = [(C.bwd_rows(s, x_key="h", dres=True), C.dw_reduce(s)) for s in sets.sets]
+        else:
+            f_calls = [(C.fwd(s),) for s in sets.sets]
+            b_calls = [(C.bwd_rows(s), C.dw_reduce(s)) for s in sets.sets]
+        (tf,) = time_calls(f_calls, sets.k, reps, 2 * sets.k, stream, burst)
+        tr, tb = time_calls(b_calls, sets.k, reps, 2 * sets.k, stream, burst)
+        (ts,) = time_calls(step_plan(C, sets, residual=res), sets.k, reps, 2 * sets.k, stream,
+                           burst)[2:]
+        fb = fwd_bytes(wl.rows, wl.H, e, residual=res)
+        bb = bwd_bytes(wl.rows, wl.H, e, dres=res)
+        rb = bwd_rows_bytes(wl.rows, wl.H, e, dres=res)
+        d = {"rows": wl.rows, "H": wl.H, "dtype": wl.dtype, "residual": res,
+             "fwd_us": round(statistics.median(tf), 3), "bwd_rows_us": round(statistics.median(tr), 3),
+             "bwd_us": round(statistics.median(tb), 3), "step_us": round(statistics.median(ts), 3),
+             "fwd_bytes": fb, "bwd_bytes": bb}
+        d["fwd_GB_s"], d["fwd_pct_peak"] = _pct(fb, d["fwd_us"])
+        d["bwd_rows_GB_s"], d["bwd_rows_pct_peak"] = _pct(rb, d["bwd_rows_us"])
+        d["bwd_GB_s"], d["bwd_pct_peak"] = _pct(bb, d["bwd_us"])
+        d["step_GB_s"], d["step_pct_peak"] = _pct(fb + bb, d["step_us"])
+        d["kernels"] = sorted({k for ks in kernel_names(C, step_plan(C, sets, residual=res)[0])
+                               for k in ks})
+        out[name] = d
+        del sets, C
+        torch.cuda.empty_cache()
+
+    # Decode rows = 1, H = 896: the one-wavefront row kernel and the split-row
+    # path with S = 1, 4, 8, 16, each 10,000 calls back to back on one stream.
+    CL = c_loops()
+    wl = synth.WORKLOADS["c3_bf16_decode_1x896"]
+    sets = Sets(wl, k=1)
+    C = Calls(sets, stream)
+    s = sets.sets[0]
+    dec, dec_k = {}, {}
+    for splits in (0, 1, 4, 8, 16):
+        partials = torch.empty(max(splits, 1), dtype=torch.float32, device="cuda")
+
+        def mk(st, partials=partials, splits=splits):
+            Cs = Calls(sets, st)
+            return Cs.fwd(s) if splits == 0 else Cs.splitrow(s, partials, splits)
+        loop = None
+        if CL is not None:
+            loop = CL.bench_fwd_loop if splits == 0 else CL.bench_splitrow_loop
+        label = "row_kernel" if splits == 0 else f"splitrow_S{splits}"
+        dec[label] = time_decode(mk, stream, loop)
+        dec_k[label] = kernel_names(C, [mk(stream)])[0]
+    out["c3_bf16_decode_1x896"] = {"rows": 1, "H": wl.H, "dtype": wl.dtype,
+                                   "us_per_call": dec, "calls": 10000, "kernels": dec_k}
+    del sets, C
+
+    gw = synth.GEMV_WORKLOADS["q_proj_bf16_1024x896"]
+    A = torch.from_numpy(gw.A().view(np.int16)).view(torch.bfloat16).cuda()
+    xv = torch.from_numpy(gw.x().view(np.int16)).view(torch.bfloat16).cuda()
+    yv = torch.empty(gw.N, dtype=torch.bfloat16, device="cuda")
+    L = B.lib()
+    gq = {}
+    for splits in gw.splits:
+        parts = torch.empty(max(B.decode_gemv_partials_count(gw.N, splits), 1), device="cuda")
+
+        def mk(st, parts=parts, splits=splits):
+            return (L.decode_gemv_splitk,
+                    (ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(xv.data_ptr()),
+                     ctypes.c_void_p(yv.data_ptr()), ctypes.c_void_p(parts.data_ptr()),
+                     parts.numel(), gw.N, gw.K, splits, B.BF16, ctypes.c_void_p(st.cuda_stream)))
+        gq[f"S{splits}"] = time_decode(mk, stream, CL.bench_gemv_loop if CL else None)
+    out["q_proj_bf16_1024x896"] = {"N": gw.N, "K": gw.K, "dtype": gw.dtype, "us_per_call": gq,
+                                   "calls": 10000}
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_decode(mk, stream, loop, ncalls=10000, per_graph=100):
+    """µs per call of the call mk(stream) made `ncalls` times back to back:
+    from a Python loop, from a loop in C (if built), and captured
+    `per_graph` to a HIP graph and replayed."""
+    import torch
+    call = mk(stream)
+    for _ in range(200):
+        run(call)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(ncalls):
+        run(call)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    out = {"python_loop": round(e0.elapsed_time(e1) * 1e3 / ncalls, 3)}
+    if loop is not None:
+        out["c_loop"] = round(time_c_loop(loop, call, ncalls, stream), 3)
+    cs = torch.cuda.Stream()
+    cs.wait_stream(stream)
+    gcall = mk(cs)
+    with torch.cuda.stream(cs):
+        for _ in range(10):
+            run(gcall)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        for _ in range(per_graph):
+            run(gcall)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(ncalls // per_graph):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    out["hip_graph"] = round(e0.elapsed_time(e1) * 1e3 / ncalls, 3)
+    del g
+    return out
+
+
+def _host_cpu():
+    """(usable cores, visible cores, CPU model) of this host."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return usable, os.cpu_count() or usable, model
+
+
+def cpu_baseline(min_seconds=10.0, sample_rows=1024):
+    """The oracle (plain C, double) on a bounded sample of the headline
+    workload: the first `sample_rows` rows of the bf16 residual 16384 x 4096
+    step (residual forward, then the backward with dres), repeated until
+    `min_seconds` have passed.  Once on one thread, then on all the cores
+    this process may use: the sample's rows split into one slice per thread,
+    each thread calling the oracle on its slice (ctypes releases the GIL for
+    the call).  GB/s counts the step's algorithmic bytes for the rows done."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import oracle
     from bwd_rmsnorm_fwd_amd import synth
 
-    wl = synth.WORKLOADS["c2_bf16_4096x4096"]
-    x = synth.to_f64(wl.x(), wl.dtype)
+    wl = synth.WORKLOADS[HEADLINE]
+    R = sample_rows
+    full_x = wl.x()
+    x = synth.to_f64(full_x[:R], wl.dtype)
+    del full_x
+    res = synth.to_f64(wl.res()[:R], wl.dtype)
+    dy = synth.to_f64(wl.dy()[:R], wl.dtype)
+    dres = synth.to_f64(wl.dres()[:R], wl.dtype)
     w = synth.to_f64(wl.w(), wl.dtype)
-    dy = synth.to_f64(wl.dy(), wl.dtype)
-    oracle.rmsnorm_fwd(x[:8], w, wl.eps)  # load / build outside the timing
-    n, t0 = 0, time.perf_counter()
-    while True:
-        y, r = oracle.rmsnorm_fwd(x, w, wl.eps)
-        oracle.rmsnorm_bwd(dy, x, w, wl.eps, rstd=r)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
-    bytes_ = (fwd_bytes(wl.rows, wl.H, 2) + bwd_bytes(wl.rows, wl.H, 2)) * n
-    del y, np
-    return {"value": round(bytes_ / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} full passes of fwd+bwd over the bf16 4096x4096 workload "
-                      f"({el:.1f} s, inputs widened to float64, single thread)",
-            "ms_per_step": round(el * 1e3 / n, 2)}
+    oracle.rmsnorm_fwd(x[:2], w, wl.eps)  # load / build outside the timing
+
+    def one(lo, hi):
+        h, _, r = oracle.rmsnorm_residual_fwd(x[lo:hi], res[lo:hi], w, wl.eps, oracle.H_BF16)
+        oracle.rmsnorm_bwd(dy[lo:hi], h, w, wl.eps, rstd=r, dres=dres[lo:hi])
+
+    def timed(fn):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                return n, el
+
+    step_bytes_per_row = (fwd_bytes(wl.rows, wl.H, 2, residual=True)
+                          + bwd_bytes(wl.rows, wl.H, 2, dres=True)) / wl.rows
+    n1, el1 = timed(lambda: one(0, R))
+    usable, visible, model = _host_cpu()
+    bounds = np.linspace(0, R, usable + 1).astype(int)
+    with ThreadPoolExecutor(max_workers=usable) as ex:
+        def all_cores():
+            list(ex.map(lambda k: one(bounds[k], bounds[k + 1]), range(usable)))
+        nn, eln = timed(all_cores)
+    gbs1 = n1 * R * step_bytes_per_row / el1 / 1e9
+    gbsn = nn * R * step_bytes_per_row / eln / 1e9
+    full_ms = lambda gbs: (step_bytes_per_row * wl.rows) / (gbs * 1e9) * 1e3
+    return {"value": round(gbsn, 4), "unit": "GB/s", "cores": usable, "kind": "oracle",
+            "sample": f"rows 0-{R - 1} of the bf16 residual 16384x4096 step (residual forward + "
+                      f"backward with dres, inputs widened to float64): {nn} passes in "
+                      f"{eln:.1f} s on {usable} threads (one row slice each)",
+            "ms_per_full_step": round(full_ms(gbsn), 1),
+            "single_thread": {"value": round(gbs1, 4), "unit": "GB/s", "cores": 1,
+                              "passes": n1, "seconds": round(el1, 1),
+                              "ms_per_full_step": round(full_ms(gbs1), 1)},
+            "host": {"usable_cores": usable, "visible_cpus": visible, "cpu_model": model,
+                     "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}}
 
 
-def load_traffic(kernel_key):
-    """HBM traffic per launch of the dominant kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
+def load_traffic(kernel_name):
+    """HBM traffic per launch of a kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    ent = d.get(kernel_key)
+    ent = d.get(kernel_name)
     if not ent or ent.get("source_hash") != kernel_source_hash():
         return None
     return ent.get("bytes_per_launch")
@@ -646,13 +864,15 @@ def counters_pass(n):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU needs a few hundred steps of load before its step time settles
-    # (measured: ~38-40 µs/step over the first 50 steps, 35 µs from ~300 on,
-    # flat to 5000), so the default warm-up is long.
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=500)
+    # The GPU needs some milliseconds of load before its clocks settle; the
+    # per-configuration table and the per-kernel bursts run first, so even a
+    # short warm-up starts from a busy GPU.
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--suite", default=None, help="also measure every workload into this file")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration table (headline step only)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-ref-mb", type=int, default=0,
                     help="after the step, run a plain device copy of this many MiB (reference "
@@ -677,11 +897,20 @@ def main():
         print(json.dumps({"counters_pass": args.counters_pass, "workloads": COUNTER_WORKLOADS,
                           "copy_ref_bytes": args.copy_ref_mb << 20}), flush=True)
         return
+    # Every configuration first (this also brings the GPU to its working
+    # clocks), then the headline step: W warm-up steps and K timed steps.
+    configs = config_table() if not args.no_configs else None
     r = bench_step(args.steps, args.warmup)
     wl = r["wl"]
     total_bytes = r["fwd_bytes"] + r["bwd_bytes"]
     value = total_bytes / (r["ms_step"] * 1e-3) / 1e9
-    ach = r["rows_bytes"] / (r["rows_us"] * 1e-6) / 1e9
+    # The dominant kernel: the longer of the residual forward and the
+    # backward row pass inside the step.
+    if r["fwd_us"] >= r["rows_us"]:
+        dom_name, dom_us, dom_bytes = r["names"][0][0], r["fwd_us"], r["fwd_bytes"]
+    else:
+        dom_name, dom_us, dom_bytes = r["names"][1][0], r["rows_us"], r["rows_bytes"]
+    ach = dom_bytes / (dom_us * 1e-6) / 1e9
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -695,9 +924,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "rmsnorm fwd+bwd bf16 rows=4096 H=4096 eps=1e-6 "
-                               "(x~N(0,1) with 41 outlier feature columns x50, w~U(0.5,1.5), "
-                               "dy~N(0,1e-2))",
+        "config": {"workload": "fused residual-add + RMSNorm fwd+bwd bf16 rows=16384 (B=4,T=4096) "
+                               "H=4096 eps=1e-6 (x,res~N(0,1), w~U(0.5,1.5), dy,dres~N(0,1e-2)); "
+                               "bwd adds dres into dh",
                    "rows": wl.rows, "H": wl.H, "cold_cache_buffer_sets": r["k"],
                    "bytes_per_step": total_bytes},
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
@@ -705,21 +934,27 @@ def main():
         "bwd_us": round(r["rows_us"] + r["reduce_us"], 3),
         "bwd_rows_us": round(r["rows_us"], 3),
         "dw_reduce_us": round(r["reduce_us"], 3),
+        "fwd_pct_peak": _pct(r["fwd_bytes"], r["fwd_us"])[1],
+        "bwd_pct_peak": _pct(r["bwd_bytes"], r["rows_us"] + r["reduce_us"])[1],
         "event_span_ms_per_step": round(r["span_ms"], 5),
-        "timing": "value/ms_per_step: wall clock over the timed steps (no per-kernel events); "
-                  "per-kernel µs: event-bracketed back-to-back launches of that kernel alone",
+        "kernels": [k for ks in r["names"] for k in ks],
+        "timing": f"value/ms_per_step: wall clock over the timed steps (no per-kernel events); "
+                  f"per-kernel µs: HIP events around a burst of {r['burst']} back-to-back "
+                  f"launches of that kernel alone, run before the warm-up steps",
         "roofline": {
-            "kernel": "bwd_rows_kernel<bf16,8,256,2,512>",
+            "kernel": dom_name,
             "bound": "hbm",
             "achieved": round(ach, 1),
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(ach / PEAK_GBS, 4),
-            "traffic": load_traffic("bwd_rows_c2"),
-            "algorithmic_bytes_per_launch": r["rows_bytes"],
-            "avg_launch_us": round(r["rows_us"], 3),
+            "traffic": load_traffic(dom_name),
+            "algorithmic_bytes_per_launch": dom_bytes,
+            "avg_launch_us": round(dom_us, 3),
         },
     }
+    if configs is not None:
+        line["configs"] = configs
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     if args.suite:

@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         "rmsnorm_status_str": ([i32], ctypes.c_char_p),
         "decode_gemv_partials_count": ([i64, i32], sz),
         "decode_gemv_splitk": ([vp, vp, vp, vp, sz, i64, i64, i32, i32, vp], i32),
+        "rmsnorm_set_dry_run": ([i32], i32),
+        "rmsnorm_dry_run_report": ([], ctypes.c_char_p),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -64,6 +66,25 @@ def lib() -> ctypes.CDLL:
 
 def status_str(status: int) -> str:
     return lib().rmsnorm_status_str(int(status)).decode()
+
+
+def rmsnorm_set_dry_run(enable: bool) -> bool:
+    return bool(lib().rmsnorm_set_dry_run(1 if enable else 0))
+
+
+def rmsnorm_dry_run_report() -> str:
+    return lib().rmsnorm_dry_run_report().decode()
+
+
+def launches_of(fn, *args) -> list:
+    """The kernels (name, grid, block lines) that calling fn(*args) launches,
+    recorded in the library's dry-run mode instead of launching them."""
+    prev = rmsnorm_set_dry_run(True)
+    try:
+        fn(*args)
+        return [l for l in rmsnorm_dry_run_report().splitlines() if l]
+    finally:
+        rmsnorm_set_dry_run(prev)
 
 
 # ---------------------------------------------------------------- marshalling helpers

@@ -90,13 +90,13 @@ template <typename T, int VEC, int TEAM>
 static hipError_t launch_team(const GemvArgs& a, hipStream_t st) {
     constexpr int RPW = 256 / TEAM;
     const dim3 grid((unsigned)((a.N + RPW - 1) / RPW), (unsigned)a.splits);
-    hipLaunchKernelGGL((gemv_splitk_kernel<T, VEC, TEAM>), grid, dim3(256), 0, st, (const T*)a.A,
+    RMS_LAUNCH((gemv_splitk_kernel<T, VEC, TEAM>), grid, dim3(256), 0, st, (const T*)a.A,
                        (const T*)a.x, (T*)a.y, a.partials, a.N, a.K, a.seg, a.splits);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_error();
     if (e != hipSuccess || a.splits == 1) return e;
-    hipLaunchKernelGGL((splitk_reduce_kernel<T>), dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0,
+    RMS_LAUNCH((splitk_reduce_kernel<T>), dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0,
                        st, (const float*)a.partials, (T*)a.y, a.N, a.splits);
-    return hipGetLastError();
+    return launch_error();
 }
 
 template <typename T, int VEC>

@@ -38,7 +38,8 @@ rmsnorm_status_t decode_gemv_splitk(const void* A, const void* x, void* y, float
     int team = 1;
     while (team < sv && team < 64) team *= 2;
     rms::GemvArgs a{A, x, y, partials, (int)N, (int)K, (int)(sv * vec), splits, team};
-    return rms::launch_gemv(dt, vec, a, stream) == hipSuccess ? RMSNORM_OK : RMSNORM_ELAUNCH;
+    const hipError_t err = rms::launch_gemv(dt, vec, a, stream);
+    return err == hipSuccess || rms::dry_run_active() ? RMSNORM_OK : RMSNORM_ELAUNCH;
 }
 
 }  // extern "C"

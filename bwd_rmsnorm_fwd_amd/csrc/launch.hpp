@@ -6,7 +6,35 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <typeinfo>
+
 namespace rms {
+
+// Dry run (rmsnorm_set_dry_run): while active on the calling host thread,
+// RMS_LAUNCH records the kernel it would launch, with its grid and block,
+// instead of launching it.
+bool dry_run_active();
+void dry_run_record(const char* pretty, dim3 grid, dim3 block);
+
+// A kernel instance's mangled name, carried by the type name of a constant
+// that holds its address (the dry run demangles it).
+template <auto K>
+const char* kernel_pretty() {
+    return typeid(std::integral_constant<decltype(K), K>).name();
+}
+
+#define RMS_LAUNCH(KERNEL, GRID, BLOCK, SHM, STREAM, ...)                          \
+    do {                                                                         \
+        if (::rms::dry_run_active())                                             \
+            ::rms::dry_run_record(::rms::kernel_pretty<&KERNEL>(), GRID, BLOCK); \
+        else                                                                     \
+            hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHM, STREAM, __VA_ARGS__);   \
+    } while (0)
+
+// The error of the last launch: hipGetLastError(), or success during a dry
+// run, which launches nothing.
+inline hipError_t launch_error() { return dry_run_active() ? hipSuccess : hipGetLastError(); }
 
 enum class DType { F32 = 0, BF16 = 1 };
 

@@ -3,11 +3,48 @@
 // host synchronisation, no printing.
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cxxabi.h>
+#include <stdlib.h>
+
+#include <string>
 
 #include "../../include/rmsnorm.h"
 #include "launch.hpp"
 
 namespace rms {
+
+// Dry-run state, per host thread.
+static thread_local bool t_dry_run = false;
+static thread_local std::string t_dry_report;
+
+bool dry_run_active() { return t_dry_run; }
+
+void dry_run_record(const char* mangled, dim3 grid, dim3 block) {
+    // The demangled type reads "std::integral_constant<void (*)(...),
+    // &(void rms::name<args>(...))>": keep "rms::name<args>".
+    int st = 0;
+    char* dem = abi::__cxa_demangle(mangled, nullptr, nullptr, &st);
+    std::string text = (st == 0 && dem) ? std::string(dem) : std::string(mangled);
+    free(dem);
+    std::string name = text;
+    const size_t b = text.find("rms::", text.find("&("));
+    if (b != std::string::npos) {
+        size_t i = text.find('<', b);
+        int depth = 0;
+        for (; i != std::string::npos && i < text.size(); ++i) {
+            if (text[i] == '<') ++depth;
+            if (text[i] == '>' && --depth == 0) break;
+        }
+        if (i != std::string::npos && i < text.size()) name = text.substr(b, i + 1 - b);
+    }
+    char dims[96];
+    snprintf(dims, sizeof dims, " grid=%ux%ux%u block=%u\n", grid.x, grid.y, grid.z, block.x);
+    t_dry_report += name;
+    t_dry_report += dims;
+}
 
 bool choose_geometry(int64_t H, int vec, bool wide, Geometry* g) {
     const int64_t n = (H + vec - 1) / vec;  // vectors per row
@@ -78,6 +115,7 @@ int pick_vec(DType dt, int64_t H, const void* const* ptrs, int n) {
 }
 
 rmsnorm_status_t launch_status(hipError_t e) {
+    if (rms::dry_run_active()) return RMSNORM_OK;  // nothing was launched
     return e == hipSuccess ? RMSNORM_OK : RMSNORM_ELAUNCH;
 }
 
@@ -89,6 +127,15 @@ size_t bwd_workspace(int64_t rows, int64_t H, DType dt) {
 }  // namespace
 
 extern "C" {
+
+int rmsnorm_set_dry_run(int enable) {
+    const int prev = rms::t_dry_run ? 1 : 0;
+    rms::t_dry_run = enable != 0;
+    if (enable) rms::t_dry_report.clear();
+    return prev;
+}
+
+const char* rmsnorm_dry_run_report(void) { return rms::t_dry_report.c_str(); }
 
 const char* rmsnorm_status_str(rmsnorm_status_t status) {
     switch (status) {

@@ -310,15 +310,15 @@ static hipError_t launch_rows_cfg(const BwdArgs& a, hipStream_t s) {
     constexpr int WGD = (TEAM >= 512 && NCH == 1) ? TEAM : (EB <= 32 ? 512 : 256);
     constexpr int WG = TEAM > WGD ? TEAM : WGD;
     if (a.dres) {
-        hipLaunchKernelGGL((bwd_rows_kernel<T, VEC, TEAM, NCH, WG, true>), dim3(a.G), dim3(WG), 0,
+        RMS_LAUNCH((bwd_rows_kernel<T, VEC, TEAM, NCH, WG, true>), dim3(a.G), dim3(WG), 0,
                            s, (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
                            (const T*)a.dres, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
     } else {
-        hipLaunchKernelGGL((bwd_rows_kernel<T, VEC, TEAM, NCH, WG, false>), dim3(a.G), dim3(WG), 0,
+        RMS_LAUNCH((bwd_rows_kernel<T, VEC, TEAM, NCH, WG, false>), dim3(a.G), dim3(WG), 0,
                            s, (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
                            (const T*)nullptr, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
     }
-    return hipGetLastError();
+    return launch_error();
 }
 
 template <typename T, int VEC>
@@ -348,13 +348,13 @@ hipError_t launch_dw_reduce(DType dt, const float* partial, int G, int ldp, int 
                             hipStream_t s) {
     const int grid = ldp / kRedCols;
     if (dt == DType::F32) {
-        hipLaunchKernelGGL((dw_reduce_kernel<float>), dim3(grid), dim3(kRedWG), 0, s, partial, G, ldp,
+        RMS_LAUNCH((dw_reduce_kernel<float>), dim3(grid), dim3(kRedWG), 0, s, partial, G, ldp,
                            H, (float*)dw);
     } else {
-        hipLaunchKernelGGL((dw_reduce_kernel<bf16_t>), dim3(grid), dim3(kRedWG), 0, s, partial, G, ldp,
+        RMS_LAUNCH((dw_reduce_kernel<bf16_t>), dim3(grid), dim3(kRedWG), 0, s, partial, G, ldp,
                            H, (bf16_t*)dw);
     }
-    return hipGetLastError();
+    return launch_error();
 }
 
 }  // namespace rms

@@ -574,12 +574,12 @@ template <typename T, int VEC, int WW, int NS>
 static hipError_t launch_wide_cfg(const BwdArgs& a, hipStream_t s) {
     auto go = [&](auto dres_c, auto rstd_c) {
         constexpr bool D = decltype(dres_c)::value, RS = decltype(rstd_c)::value;
-        hipLaunchKernelGGL((bwd_rows_wide_kernel<T, VEC, WW, NS, D, RS>), dim3(a.G), dim3(WW), 0, s,
+        RMS_LAUNCH((bwd_rows_wide_kernel<T, VEC, WW, NS, D, RS>), dim3(a.G), dim3(WW), 0, s,
                            (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd,
                            (const T*)a.dres, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
     };
     bwd_variant(a, go);
-    return hipGetLastError();
+    return launch_error();
 }
 
 template <typename T, int VEC>
@@ -588,15 +588,15 @@ static hipError_t launch_rows_wide(const BwdArgs& a, hipStream_t s) {
     if constexpr (VEC > 1 && RMS_BWD_LDSROW) {
         if (n1024 <= 4 && !a.dres) {
             if (a.rstd) {
-                hipLaunchKernelGGL((bwd_rows_ldsrow_kernel<T, VEC, 512, 8, true>), dim3(a.G),
+                RMS_LAUNCH((bwd_rows_ldsrow_kernel<T, VEC, 512, 8, true>), dim3(a.G),
                                    dim3(512), 0, s, (const T*)a.dy, (const T*)a.x, (const T*)a.w,
                                    a.rstd, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
             } else {
-                hipLaunchKernelGGL((bwd_rows_ldsrow_kernel<T, VEC, 512, 8, false>), dim3(a.G),
+                RMS_LAUNCH((bwd_rows_ldsrow_kernel<T, VEC, 512, 8, false>), dim3(a.G),
                                    dim3(512), 0, s, (const T*)a.dy, (const T*)a.x, (const T*)a.w,
                                    a.rstd, (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
             }
-            return hipGetLastError();
+            return launch_error();
         }
     }
     if (n1024 <= 4) return launch_wide_cfg<T, VEC, 1024, 4>(a, s);
@@ -615,12 +615,12 @@ template <typename T, int VEC>
 static hipError_t launch_rows_staged(const BwdArgs& a, hipStream_t s) {
     auto go = [&](auto dres_c, auto rstd_c) {
         constexpr bool D = decltype(dres_c)::value, RS = decltype(rstd_c)::value;
-        hipLaunchKernelGGL((bwd_rows_staged_kernel<T, VEC, D, RS>), dim3(a.G), dim3(1024), 0, s,
+        RMS_LAUNCH((bwd_rows_staged_kernel<T, VEC, D, RS>), dim3(a.G), dim3(1024), 0, s,
                            (const T*)a.dy, (const T*)a.x, (const T*)a.w, a.rstd, (const T*)a.dres,
                            (T*)a.dx, a.partial, a.rows, a.H, a.ldp, a.eps);
     };
     bwd_variant(a, go);
-    return hipGetLastError();
+    return launch_error();
 }
 
 hipError_t launch_bwd_wide(DType dt, int vec, const BwdArgs& a, hipStream_t s) {

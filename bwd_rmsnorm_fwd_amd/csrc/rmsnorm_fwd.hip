@@ -201,15 +201,15 @@ static hipError_t launch_cfg(const FwdArgs& a, bool residual, hipStream_t s) {
     if (want > RMS_FWD_MAX_GRID) want = RMS_FWD_MAX_GRID;
     const int grid = (int)(nrb < want ? nrb : want);
     if (residual) {
-        hipLaunchKernelGGL((fwd_kernel<T, VEC, TEAM, NCH, WG, true>), dim3(grid), dim3(WG), 0, s,
+        RMS_LAUNCH((fwd_kernel<T, VEC, TEAM, NCH, WG, true>), dim3(grid), dim3(WG), 0, s,
                            (const T*)a.x, (const T*)a.res, (const T*)a.w, (T*)a.h, (T*)a.y, a.rstd,
                            a.rows, a.H, a.eps);
     } else {
-        hipLaunchKernelGGL((fwd_kernel<T, VEC, TEAM, NCH, WG, false>), dim3(grid), dim3(WG), 0, s,
+        RMS_LAUNCH((fwd_kernel<T, VEC, TEAM, NCH, WG, false>), dim3(grid), dim3(WG), 0, s,
                            (const T*)a.x, (const T*)nullptr, (const T*)a.w, (T*)nullptr, (T*)a.y,
                            a.rstd, a.rows, a.H, a.eps);
     }
-    return hipGetLastError();
+    return launch_error();
 }
 
 template <typename T, int VEC>

@@ -71,14 +71,14 @@ template <typename T, int VEC>
 static hipError_t launch_split(const FwdArgs& a, float* partials, int splits, hipStream_t s) {
     const int n = (a.H + VEC - 1) / VEC;
     const int chunk = ((n + splits - 1) / splits) * VEC;
-    hipLaunchKernelGGL((split_sumsq_kernel<T, VEC>), dim3((unsigned)a.rows, splits), dim3(64), 0, s,
+    RMS_LAUNCH((split_sumsq_kernel<T, VEC>), dim3((unsigned)a.rows, splits), dim3(64), 0, s,
                        (const T*)a.x, partials, a.H, chunk, splits);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_error();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((split_finalize_kernel<T, VEC, 128>), dim3((unsigned)a.rows), dim3(128), 0, s,
+    RMS_LAUNCH((split_finalize_kernel<T, VEC, 128>), dim3((unsigned)a.rows), dim3(128), 0, s,
                        (const T*)a.x, (const T*)a.w, (const float*)partials, (T*)a.y, a.rstd, a.H,
                        splits, a.eps);
-    return hipGetLastError();
+    return launch_error();
 }
 
 hipError_t launch_splitrow(DType dt, int vec, const FwdArgs& a, float* partials, int splits,

@@ -178,6 +178,22 @@ rmsnorm_status_t rmsnorm_fwd_splitrow(const void *x, const void *w, void *y, flo
 /* Static description of a status code.  Never NULL. */
 const char *rmsnorm_status_str(rmsnorm_status_t status);
 
+/* Dry run, per calling host thread (an introspection aid for benchmarks,
+ * profilers and tests; not part of any passage of the sources).  While
+ * enabled, every entry point of this library (decode_gemv_splitk included)
+ * validates its arguments exactly as usual and returns the same status, but
+ * instead of launching a kernel it appends one line per kernel it would
+ * launch to a per-thread report:
+ *     <kernel name with its template arguments> grid=<x>x<y>x<z> block=<n>
+ * No device memory is touched and nothing is enqueued.  Returns the previous
+ * setting (0 or 1); enabling clears the report. */
+int rmsnorm_set_dry_run(int enable);
+
+/* The calling thread's dry-run report since dry run was last enabled (an
+ * empty string if nothing was recorded).  Owned by the library; valid until
+ * the next call of any entry point on this thread. */
+const char *rmsnorm_dry_run_report(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -141,6 +141,71 @@ def _check_gemv_validation():
     assert f(MIS, A, A, None, 0, 8, 896, 1, B.BF16, None) == B.EALIGN
 
 
+def _dry(fn, *args):
+    B.rmsnorm_set_dry_run(True)
+    try:
+        st = fn(*args)
+        return st, [l for l in B.rmsnorm_dry_run_report().splitlines() if l]
+    finally:
+        B.rmsnorm_set_dry_run(False)
+
+
+def _check_dispatch_of_workloads():
+    """Which kernels each configured workload launches (dry run: validated as
+    usual, recorded instead of launched), and the launch shapes that carry the
+    design: one team per row, several rows per wavefront for narrow rows, at
+    most one backward workgroup per CU, S split workgroups for decode."""
+    L = B.lib()
+    A = ctypes.c_void_p(0x10000)
+    eps = ctypes.c_float(1e-6)
+
+    def fwd(rows, H, dt):
+        return _dry(L.rmsnorm_fwd, A, A, A, A, rows, H, eps, dt, None)
+
+    def bwd(rows, H, dt, dres=None, rstd=A):
+        need = L.rmsnorm_bwd_workspace_bytes(rows, H, dt)
+        return _dry(L.rmsnorm_bwd, A, A, A, rstd, dres, A, A, A, need, rows, H, eps, dt, None)
+
+    def grid(line):
+        return int(line.split("grid=")[1].split("x")[0])
+
+    # c1 fp32 64 x 896; c2 bf16 4096 x 4096; c5a 262144 x 128; c5b 8192 x 8192.
+    for rows, H, dt, t in ((64, 896, B.F32, "float, 4"), (4096, 4096, B.BF16, "unsigned short, 8"),
+                           (262144, 128, B.BF16, "unsigned short, 8"),
+                           (8192, 8192, B.BF16, "unsigned short, 8")):
+        st, f = fwd(rows, H, dt)
+        assert st == B.OK and len(f) == 1 and f[0].startswith(f"rms::fwd_kernel<{t},"), f
+        st, b = bwd(rows, H, dt)
+        assert st == B.OK and len(b) == 2, b
+        assert "bwd_rows" in b[0] and f"<{t}," in b[0] and "dw_reduce_kernel" in b[1], b
+        assert grid(b[0]) <= 256, b                      # at most one workgroup per CU
+    # Narrow rows: a 16-lane team per 128-wide bf16 row, 4 rows per wavefront.
+    assert "rms::fwd_kernel<unsigned short, 8, 16, 1," in fwd(262144, 128, B.BF16)[1][0]
+    assert "rms::bwd_rows_kernel<unsigned short, 8, 16, 1," in bwd(262144, 128, B.BF16)[1][0]
+    # c4: residual forward and the backward with dres.
+    st, f = _dry(L.rmsnorm_residual_fwd, A, A, A, A, A, A, 16384, 4096, eps, B.BF16, None)
+    assert st == B.OK and len(f) == 1 and f[0].startswith("rms::fwd_kernel<unsigned short, 8,")
+    assert f[0].split(" grid=")[0].endswith("true>"), f
+    st, b = bwd(16384, 4096, B.BF16, dres=A)
+    assert st == B.OK and b[0].split(" grid=")[0].endswith("true>"), b
+    # c3 decode: S split workgroups, then one partial-reduce workgroup.
+    for S in (1, 4, 8, 16):
+        st, d = _dry(L.rmsnorm_fwd_splitrow, A, A, A, A, A, S, 1, 896, eps, S, B.BF16, None)
+        assert st == B.OK and len(d) == 2, d
+        assert d[0].startswith("rms::split_sumsq_kernel") and f"grid=1x{S}x1" in d[0], d
+        assert d[1].startswith("rms::split_finalize_kernel") and "grid=1x1x1" in d[1], d
+    # Wide rows: the LDS-staged, row-in-LDS and streaming backward kernels.
+    assert "bwd_rows_staged_kernel" in bwd(2730, 12288, B.BF16)[1][0]
+    assert "bwd_rows_ldsrow_kernel" in bwd(2048, 32768, B.BF16)[1][0]
+    assert "bwd_rows_wide_kernel" in bwd(2048, 32768, B.BF16, dres=A)[1][0]
+    assert "bwd_rows_wide_kernel" in bwd(1024, 65536, B.BF16)[1][0]
+    # rows = 0: nothing to launch for the forward; the backward still writes dw.
+    assert fwd(0, 4096, B.BF16) == (B.OK, [])
+    # A call that fails validation records nothing.
+    st, d = _dry(L.rmsnorm_fwd, A, A, A, A, 4, 64, ctypes.c_float(-1.0), B.BF16, None)
+    assert st == B.EINVAL and d == []
+
+
 HIDDEN_ENV = {"HIP_VISIBLE_DEVICES": "-1", "ROCR_VISIBLE_DEVICES": "-1", "CUDA_VISIBLE_DEVICES": "-1"}
 
 CHILD = r"""
@@ -159,7 +224,8 @@ print("ok")
 
 
 @pytest.mark.parametrize("check", ["_check_fwd_validation", "_check_bwd_validation_and_workspace",
-                                   "_check_splitrow_validation", "_check_gemv_validation"])
+                                   "_check_splitrow_validation", "_check_gemv_validation",
+                                   "_check_dispatch_of_workloads"])
 def test_validation_without_a_device(check):
     env = dict(os.environ, **HIDDEN_ENV)
     code = CHILD.format(tests=os.path.dirname(os.path.abspath(__file__)), root=ROOT, fn=check)
