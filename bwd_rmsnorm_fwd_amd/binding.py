@@ -16,7 +16,8 @@ import os
 
 from ._build import LIB_PATH
 
-OK, EINVAL, EALIGN, EWORKSPACE, EUNSUPPORTED, ELAUNCH = range(6)
+OK, EINVAL, EALIGN, EWORKSPACE, EUNSUPPORTED, ELAUNCH, ESCRATCH = range(7)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 F32, BF16 = 0, 1
 MAX_H = 65536
 MAX_H_SCALAR = 16384
@@ -53,6 +54,7 @@ def lib() -> ctypes.CDLL:
         "rmsnorm_status_str": ([i32], ctypes.c_char_p),
         "decode_gemv_partials_count": ([i64, i32], sz),
         "decode_gemv_splitk": ([vp, vp, vp, vp, sz, i64, i64, i32, i32, vp], i32),
+        "rmsnorm_bwd_noalloc": ([vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp], i32),
         "rmsnorm_set_dry_run": ([i32], i32),
         "rmsnorm_dry_run_report": ([], ctypes.c_char_p),
     }
@@ -195,6 +197,18 @@ def rmsnorm_bwd(dy, x, w, rstd, dres, dx, dw, workspace, eps: float = 1e-6, stre
            lib().rmsnorm_bwd(_p(dy), _p(x), _p(w), _p(rstd), _p(dres), _p(dx), _p(dw),
                              _p(workspace), nbytes, rows, H, float(eps), _dtype_code(x),
                              _stream(stream)))
+
+
+def rmsnorm_bwd_noalloc(dy, x, w, rstd, dres, dx, dw, eps: float = 1e-6, stream=None) -> None:
+    """As rmsnorm_bwd, with the dw partial sums in the library's static device
+    scratch instead of a caller workspace (no allocation anywhere)."""
+    _contig(dy, x, w, rstd, dres, dx, dw)
+    rows, H = _rows_h(x)
+    _bwd_expect(dy, x, w, rstd, dres, dx, rows, H)
+    _expect("dw", dw, H, x.dtype)
+    _check("rmsnorm_bwd_noalloc",
+           lib().rmsnorm_bwd_noalloc(_p(dy), _p(x), _p(w), _p(rstd), _p(dres), _p(dx), _p(dw),
+                                     rows, H, float(eps), _dtype_code(x), _stream(stream)))
 
 
 def rmsnorm_bwd_rows(dy, x, w, rstd, dres, dx, workspace, eps: float = 1e-6, stream=None) -> None:

@@ -9,6 +9,7 @@
 #include <cxxabi.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <string>
 
 #include "../../include/rmsnorm.h"
@@ -89,6 +90,13 @@ int choose_vec(DType dt, int64_t H, const void* const* ptrs, int nptrs) {
 
 using rms::DType;
 
+// The scratch behind rmsnorm_bwd_noalloc: one copy per GPU, in the code
+// object's device memory, for the life of the process.  In host code
+// `scratch` names a host-side stand-in, never the device array: its device
+// address on each GPU comes from hipGetSymbolAddress, looked up on that GPU's
+// first call and kept in g_scratch_dev; every use goes through that pointer.
+static __device__ __align__(256) float scratch[RMSNORM_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
 namespace {
 
 bool valid_dtype(rmsnorm_dtype_t dt) { return dt == RMSNORM_F32 || dt == RMSNORM_BF16; }
@@ -124,6 +132,26 @@ size_t bwd_workspace(int64_t rows, int64_t H, DType dt) {
     return (size_t)G * (size_t)rms::partial_ld(H) * sizeof(float);
 }
 
+constexpr size_t kScratchBytes = RMSNORM_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_dev[kMaxDevices];
+
+rmsnorm_status_t scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RMSNORM_ELAUNCH;
+    void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // With `dev` current: its own copy of the array.
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();  // leave no sticky error behind
+            return RMSNORM_ELAUNCH;
+        }
+        g_scratch_dev[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return RMSNORM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,6 +173,7 @@ const char* rmsnorm_status_str(rmsnorm_status_t status) {
         case RMSNORM_EWORKSPACE: return "workspace missing or too small";
         case RMSNORM_EUNSUPPORTED: return "unsupported shape";
         case RMSNORM_ELAUNCH: return "kernel launch failed";
+        case RMSNORM_ESCRATCH: return "shape needs more than the library's static scratch";
     }
     return "unknown status";
 }
@@ -255,6 +284,27 @@ rmsnorm_status_t rmsnorm_bwd(const void* dy, const void* x, const void* w, const
         if (st != RMSNORM_OK) return st;
     }
     return dw_reduce_common(workspace, workspace_bytes, dw, rows, H, dtype, stream);
+}
+
+rmsnorm_status_t rmsnorm_bwd_noalloc(const void* dy, const void* x, const void* w,
+                                     const float* rstd, const void* dres, void* dx, void* dw,
+                                     int64_t rows, int64_t H, float eps, rmsnorm_dtype_t dtype,
+                                     hipStream_t stream) {
+    rmsnorm_status_t st = check_shape(rows, H, eps, dtype);
+    if (st != RMSNORM_OK) return st;
+    if (!dw) return RMSNORM_EINVAL;
+    const size_t need = bwd_workspace(rows, H, to_dt(dtype));
+    if (need > kScratchBytes) return RMSNORM_ESCRATCH;
+    void* ws = nullptr;
+    if (need > 0) {
+        if (rms::dry_run_active()) {
+            ws = reinterpret_cast<void*>(uintptr_t{256});  // nothing is launched
+        } else {
+            st = scratch_address(&ws);
+            if (st != RMSNORM_OK) return st;
+        }
+    }
+    return rmsnorm_bwd(dy, x, w, rstd, dres, dx, dw, ws, need, rows, H, eps, dtype, stream);
 }
 
 size_t rmsnorm_splitrow_partials_count(int64_t rows, int splits) {

@@ -74,7 +74,9 @@ typedef enum {
     RMSNORM_EWORKSPACE = 3,   /* workspace/partials missing or smaller than required */
     RMSNORM_EUNSUPPORTED = 4, /* H > RMSNORM_MAX_H, or H / vector width too large
                                  for the scalar path (see RMSNORM_MAX_H_SCALAR) */
-    RMSNORM_ELAUNCH = 5       /* HIP reported an error for a kernel launch */
+    RMSNORM_ELAUNCH = 5,      /* HIP reported an error for a kernel launch */
+    RMSNORM_ESCRATCH = 6      /* rmsnorm_bwd_noalloc: the shape needs more than the
+                                 library's static scratch (RMSNORM_NOALLOC_SCRATCH_BYTES) */
 } rmsnorm_status_t;
 
 /* Largest row width.  Rows that miss the 128-bit path (odd H, unaligned
@@ -153,6 +155,33 @@ rmsnorm_status_t rmsnorm_bwd_rows(const void *dy, const void *x, const void *w,
 rmsnorm_status_t rmsnorm_bwd_dw_reduce(const void *workspace, size_t workspace_bytes,
                                        void *dw, int64_t rows, int64_t H,
                                        rmsnorm_dtype_t dtype, hipStream_t stream);
+
+/* Bytes of the static device scratch behind rmsnorm_bwd_noalloc (one copy per
+ * GPU the library runs on, held until the process ends): 256 partial rows of
+ * 16384 floats, which covers every shape with H <= 16384, and wider rows
+ * when rows is small enough (the need is rmsnorm_bwd_workspace_bytes). */
+#define RMSNORM_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* Backward for callers that cannot allocate device memory: code recorded
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Computes exactly what rmsnorm_bwd computes, with the same
+ * kernels and reduction order (dx and dw bitwise equal to rmsnorm_bwd's),
+ * but takes no workspace: the dw partial sums go to a scratch array that the
+ * library holds in device memory, RMSNORM_NOALLOC_SCRATCH_BYTES per GPU.
+ *   Arguments as for rmsnorm_bwd, without workspace/workspace_bytes.
+ *   Returns RMSNORM_ESCRATCH, enqueuing nothing, when
+ *   rmsnorm_bwd_workspace_bytes(rows, H, dtype) > RMSNORM_NOALLOC_SCRATCH_BYTES,
+ *   and RMSNORM_ELAUNCH if HIP cannot give the scratch's device address.
+ * No allocation of any kind: the scratch's address on the current device is
+ * looked up once (hipGetSymbolAddress) on that device's first call.  Every
+ * call on a GPU shares that GPU's one scratch array (the row pass overwrites
+ * every partial the reduce pass reads, so nothing needs clearing): calls on
+ * one GPU must not overlap in time (different streams or host threads
+ * without ordering between them race on the scratch). */
+rmsnorm_status_t rmsnorm_bwd_noalloc(const void *dy, const void *x, const void *w,
+                                     const float *rstd, const void *dres,
+                                     void *dx, void *dw, int64_t rows, int64_t H, float eps,
+                                     rmsnorm_dtype_t dtype, hipStream_t stream);
 
 /* Floats of partial sums rmsnorm_fwd_splitrow needs: rows * splits. */
 size_t rmsnorm_splitrow_partials_count(int64_t rows, int splits);
