@@ -40,7 +40,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (% of MI355X peak) + µs/call, RMSNorm fwd and bwd"
 PEAK_GBS = 8000.0          # MI355X HBM3E
-COLD_BYTES = 1 << 30       # distinct memory touched by consecutive steps
+# Input bytes read by other calls between two uses of one buffer set: 2.5 x
+# the 256 MB Infinity Cache.  Measured on the bf16 forwards with cached
+# loads: with less, a call still finds part of its inputs there (8192 x 8192
+# with 134 MB read in between: 86.5% of 8 TB/s; with 402 MB or more: 74%;
+# 4096 x 4096 with 235 MB read in between: 73.7%, with 369 MB: 62.6%).
+# Nontemporal loads do not allocate there (the backward's times do not
+# depend on the number of sets), but the rule does not rely on it.
+COLD_BYTES = 640 << 20
+MAX_SETS = 64
 
 
 # ---------------------------------------------------------------- algorithmic bytes
@@ -74,7 +82,11 @@ def kernel_source_hash():
 # ---------------------------------------------------------------- device plumbing
 
 class Sets:
-    """K rotating buffer sets of one workload, filled with its seeded inputs."""
+    """K rotating buffer sets of one workload, filled with its seeded inputs.
+    K is chosen so that between two uses of one set the other sets' calls of
+    the kernel that reads least (the forward: x, and res) read at least
+    COLD_BYTES: no call finds its inputs in the Infinity Cache.  (At most
+    MAX_SETS: the smallest workload is launch-bound either way.)"""
 
     def __init__(self, wl, k=None, residual=False, dres=False):
         import numpy as np
@@ -96,10 +108,9 @@ class Sets:
         x, w, dy = dev(wl.x()), dev(wl.w()), dev(wl.dy())
         res = dev(wl.res()) if residual else None
         dres_t = dev(wl.dres()) if dres else None
-        n = rows * H
         ws_bytes = max(B.rmsnorm_bwd_workspace_bytes(rows, H, self.code), 16)
-        set_bytes = n * self.e * (4 + (2 if residual else 0) + (1 if dres else 0)) + ws_bytes
-        self.k = k or max(2, math.ceil(COLD_BYTES / set_bytes))
+        read = rows * H * self.e * (2 if residual else 1)
+        self.k = k or min(MAX_SETS, max(2, math.ceil(COLD_BYTES / read) + 1))
         self.sets = []
         for _ in range(self.k):
             s = {

@@ -134,11 +134,13 @@ __device__ __forceinline__ V team_sum_nofence(V v, V* lds) {
 
 // The workgroup's dw partial row from the column sums of its R = WG / TEAM
 // teams (lane lt of a team holds columns (c * TEAM + lt) * VEC + k).  The
-// teams are combined in team order through comb: side by side ([R][HT],
-// summed per column) when that fits in 32 KiB, else one after another into
-// a single [HT] row.  With VEC > 1, H is a multiple of VEC, so groups of four
-// columns that start below H end below H (and below HT); ldp is a multiple
-// of 64.
+// teams are combined in team order through comb: side by side (summed per
+// column) when that fits in 32 KiB, else one after another into a single
+// row.  With VEC >= 4 the side-by-side layout is [team][chunk][group of four
+// columns][lane] float4, so the lanes of a 128-bit LDS access are 16 bytes
+// apart (no bank conflicts; the lane-major [team][column] layout put them 32
+// bytes apart).  With VEC > 1, H is a multiple of VEC, so groups of four
+// columns that start below H end below H; ldp is a multiple of 64.
 template <int VEC, int TEAM, int NCH, int WG>
 struct PartialComb {
     static constexpr int R = WG / TEAM;
@@ -175,6 +177,30 @@ __device__ __forceinline__ void write_partial(const float (&acc)[NCH][VEC], floa
                 }
             }
         }
+    } else if constexpr (PC::kWide && VEC >= 4) {
+        constexpr int NQ = VEC / 4;
+        float4* c4 = reinterpret_cast<float4*>(comb);  // [R][NCH][NQ][TEAM]
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                c4[((team * NCH + c) * NQ + q) * TEAM + lt] =
+                    make_float4(acc[c][4 * q], acc[c][4 * q + 1], acc[c][4 * q + 2], acc[c][4 * q + 3]);
+        }
+        __syncthreads();
+        constexpr int NG = NCH * NQ * TEAM;  // float4 groups per team
+        for (int i = tid; i < NG; i += WG) {
+            const int c = i / (NQ * TEAM), q = (i / TEAM) % NQ, l = i % TEAM;
+            const int col = (c * TEAM + l) * VEC + 4 * q;
+            if (col < H) {
+                float4 sum = c4[i];
+                for (int t = 1; t < R; ++t) {
+                    const float4 v = c4[t * NG + i];
+                    sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+                }
+                store4(col, sum.x, sum.y, sum.z, sum.w);
+            }
+        }
     } else if constexpr (PC::kWide) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
@@ -182,21 +208,10 @@ __device__ __forceinline__ void write_partial(const float (&acc)[NCH][VEC], floa
             for (int k = 0; k < VEC; ++k) comb[team * HT + (c * TEAM + lt) * VEC + k] = acc[c][k];
         }
         __syncthreads();
-        if constexpr (VEC >= 4) {
-            for (int col = tid * 4; col < H; col += WG * 4) {
-                float4 sum = *reinterpret_cast<const float4*>(comb + col);
-                for (int t = 1; t < R; ++t) {
-                    const float4 v = *reinterpret_cast<const float4*>(comb + t * HT + col);
-                    sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
-                }
-                store4(col, sum.x, sum.y, sum.z, sum.w);
-            }
-        } else {
-            for (int col = tid; col < H && col < HT; col += WG) {
-                float sum = comb[col];
-                for (int t = 1; t < R; ++t) sum += comb[t * HT + col];
-                prow[col] = sum;
-            }
+        for (int col = tid; col < H && col < HT; col += WG) {
+            float sum = comb[col];
+            for (int t = 1; t < R; ++t) sum += comb[t * HT + col];
+            prow[col] = sum;
         }
     } else {
         for (int t = 0; t < R; ++t) {

@@ -100,6 +100,15 @@ __device__ __forceinline__ Pack<T, VEC> zero_pack() {
     return r;
 }
 
+// Makes p's value opaque to the optimiser (an empty asm that may "change"
+// it), so that values derived from p are recomputed after this point rather
+// than kept live from before it, and nothing derived from p is hoisted out of
+// a loop that calls this.
+template <typename T, int VEC>
+__device__ __forceinline__ void opaque(Pack<T, VEC>& p) {
+    asm volatile("" : "+v"(p.v));
+}
+
 template <typename T, int VEC>
 __device__ __forceinline__ void unpack(const Pack<T, VEC>& p, float (&f)[VEC]) {
     if constexpr (sizeof(T) == 4 && VEC == 4) {
@@ -220,11 +229,17 @@ __device__ __forceinline__ void buf_store_vec(BufRes r, uint32_t off, const floa
     }
 }
 
-// Products for the per-row fp64 sums.  For bf16 inputs the fp32 products are
-// exact (8-bit significands: a square has 16 bits, w*dy*x has 24), so the
-// fp32 multiply loses nothing; for fp32 inputs they are formed in fp64.
+// Products for the per-row fp64 sums.  Squares are formed in fp64 (the
+// caller's add contracts with the multiply into one fp64 fused multiply-add):
+// exact for every fp32 or bf16 value, and free of the overflow (|x| beyond
+// about 2^64) and underflow (|x| below about 2^-63) of an fp32 square.  For
+// bf16 inputs w*dy*x is formed in fp32, where it is exact (8-bit significands:
+// 24 bits in all) while |w dy x| lies between 2^-126 and 2^128, the range
+// include/rmsnorm.h states; for fp32 inputs it is formed in fp64.  (Forming
+// it in fp64 for bf16 as well raised the register use of the row-in-LDS
+// backward until it spilled.)
 __device__ __forceinline__ double sq64(float v, float*) { return (double)v * (double)v; }
-__device__ __forceinline__ double sq64(float v, bf16_t*) { return (double)(v * v); }
+__device__ __forceinline__ double sq64(float v, bf16_t*) { return (double)v * (double)v; }
 __device__ __forceinline__ double prod2_64(float a, float b, float*) {
     return (double)a * (double)b;
 }
@@ -240,10 +255,11 @@ __device__ __forceinline__ double prod3_64(float a, float b, float c, bf16_t*) {
 // refined by one Newton step r' = r (3 - m r^2) / 2, which squares its
 // relative error, leaving r within a few fp64 ulps (so its fp32 rounding is
 // the correctly rounded fp32 of the exact value except on exact ties).  About
-// a fifth of the instructions of 1.0 / sqrt(m).  m = 0 returns +inf.
+// a fifth of the instructions of 1.0 / sqrt(m).  m = 0 returns +inf and
+// m = +inf returns 0 (the hardware value; the Newton step would give NaN).
 __device__ __forceinline__ double rsqrt_f64(double m) {
     const double r = __builtin_amdgcn_rsq(m);
-    return m > 0.0 ? r * (1.5 - 0.5 * m * (r * r)) : r;
+    return (m > 0.0 && m < __builtin_inf()) ? r * (1.5 - 0.5 * m * (r * r)) : r;
 }
 
 // ---------------------------------------------------------------------------

@@ -219,37 +219,39 @@ __global__ __launch_bounds__(WG) void bwd_rows_kernel(const T* dy, const T* __re
 }
 
 // dw[j] = sum_{g < G} partial[g][j] in a fixed order.  A workgroup of
-// kRedWG lanes owns kRedCols columns (kRedCL lanes x 4 columns, 128-bit
-// loads) and kRedGL lanes over g: lane gl adds rows g = gl, gl + kRedGL, ...
-// in increasing g, kRedU independent loads in flight per step (rows past G
-// load as zero, which leaves the sum unchanged), then the kRedGL lane sums of
-// each column are added in gl order.
-#ifndef RMS_RED_CL
-#define RMS_RED_CL 8
-#endif
-#ifndef RMS_RED_WG
-#define RMS_RED_WG 256
-#endif
+// kRedWG lanes owns kRedCols = 32 columns: lane t takes the four columns
+// 4 (t % 8) .. + 3 (one 128-bit load per partial row) and the partial rows
+// g = gl, gl + 32, gl + 64, ... with gl = t / 8, adding them in increasing g
+// with all of its loads in flight at once (rows past G load as zero, which
+// leaves the sum unchanged).  The 32 gl sums of a column are then added as a
+// tree: across the 8 gl of a wavefront by lane exchanges (xor 8, 16, 32:
+// both partners form the same sum, a + b == b + a), then the 4 wavefronts'
+// sums through LDS in wave order.  The order depends on G alone.
 #ifndef RMS_RED_UNROLL
 #define RMS_RED_UNROLL 8
 #endif
-constexpr int kRedCL = RMS_RED_CL;
-constexpr int kRedWG = RMS_RED_WG;
+constexpr int kRedWG = 256;
+constexpr int kRedCL = 8;                  // column lanes (4 columns each)
+constexpr int kRedGL = kRedWG / kRedCL;    // 32 partial-row lanes
+constexpr int kRedCols = 4 * kRedCL;       // 32 columns per workgroup
 constexpr int kRedU = RMS_RED_UNROLL;
-constexpr int kRedGL = kRedWG / kRedCL;
-constexpr int kRedCols = 4 * kRedCL;
-static_assert(kRedWG % kRedCL == 0 && 64 % kRedCols == 0, "reduce tile must divide ldp (multiple of 64)");
+static_assert(64 % kRedCols == 0, "reduce tile must divide ldp (multiple of 64)");
+
+__device__ __forceinline__ float shfl_xor_f32(float v, int m) {
+    const int src = (int)(threadIdx.x % kWave) ^ m;
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
 
 template <typename T>
 __global__ __launch_bounds__(kRedWG) void dw_reduce_kernel(const float* __restrict__ partial, int G,
                                                            int ldp, int H, T* __restrict__ dw) {
-    __shared__ float part[kRedGL][kRedCols + 1];
+    __shared__ float4 part[kRedWG / kWave][kRedCL];
     const int cl = threadIdx.x % kRedCL;
     const int gl = threadIdx.x / kRedCL;
     // ldp is a multiple of 64 and of kRedCols, so col0 + 3 < ldp for every workgroup.
     const int col0 = blockIdx.x * kRedCols + cl * 4;
     const float* base = partial + col0;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int g = gl; g < G; g += kRedU * kRedGL) {
         float4 p[kRedU];
 #pragma unroll
@@ -259,18 +261,26 @@ __global__ __launch_bounds__(kRedWG) void dw_reduce_kernel(const float* __restri
                           : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
-        for (int u = 0; u < kRedU; ++u) { a0 += p[u].x; a1 += p[u].y; a2 += p[u].z; a3 += p[u].w; }
+        for (int u = 0; u < kRedU; ++u) { a.x += p[u].x; a.y += p[u].y; a.z += p[u].z; a.w += p[u].w; }
     }
-    part[gl][cl * 4 + 0] = a0;
-    part[gl][cl * 4 + 1] = a1;
-    part[gl][cl * 4 + 2] = a2;
-    part[gl][cl * 4 + 3] = a3;
+    // Lanes cl + 8 j (j = 0..7) of a wavefront hold the same columns.
+#pragma unroll
+    for (int m = 8; m < kWave; m <<= 1) {
+        a.x += shfl_xor_f32(a.x, m);
+        a.y += shfl_xor_f32(a.y, m);
+        a.z += shfl_xor_f32(a.z, m);
+        a.w += shfl_xor_f32(a.w, m);
+    }
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x % kWave) < kRedCL) part[wave][cl] = a;
     __syncthreads();
     if (threadIdx.x < kRedCols) {
+        const int c4 = threadIdx.x / 4, k = threadIdx.x % 4;
+        const float* p0 = reinterpret_cast<const float*>(&part[0][c4]);
+        float sum = p0[k];
+#pragma unroll
+        for (int v = 1; v < kRedWG / kWave; ++v) sum += reinterpret_cast<const float*>(&part[v][c4])[k];
         const int col = blockIdx.x * kRedCols + threadIdx.x;
-        float sum = part[0][threadIdx.x];
-#pragma unroll 16
-        for (int j = 1; j < kRedGL; ++j) sum += part[j][threadIdx.x];
         if (col < H) {
             float o[1] = {sum};
             store_vec<T, 1>(dw + col, o);
@@ -332,7 +342,10 @@ static hipError_t dispatch_rows(const BwdArgs& a, hipStream_t s) {
     if (g.team == TM && g.nch == NC) return launch_rows_cfg<T, VEC, TM, NC>(a, s);
     RMS_CASE(1, 1) RMS_CASE(2, 1) RMS_CASE(4, 1) RMS_CASE(8, 1) RMS_CASE(16, 1) RMS_CASE(32, 1)
     RMS_CASE(64, 1) RMS_CASE(64, 2) RMS_CASE(128, 2) RMS_CASE(256, 2) RMS_CASE(512, 1)
-    RMS_CASE(512, 2) RMS_CASE(1024, 2)
+    RMS_CASE(512, 2)
+    // With 128-bit access the 1024 x 2 tile goes to the LDS-staged kernel
+    // above, so the register tile is built for the scalar path only.
+    if constexpr (VEC == 1) { RMS_CASE(1024, 2) }
 #undef RMS_CASE
     return hipErrorInvalidValue;
 }

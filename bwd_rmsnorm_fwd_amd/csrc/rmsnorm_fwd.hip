@@ -33,10 +33,12 @@
 #define RMS_FWD_MAX_GRID (1 << 20)
 #endif
 // Streaming (nontemporal) access to the row tensors: x/res loads, y/h
-// stores.  Measured best: stores only for the plain forward, loads and
-// stores for the residual forward.
+// stores.  Measured best with inputs that are not in the Infinity Cache:
+// loads and stores (cached loads: bf16 4096 x 4096 12.4 -> 13.5 us, 262144
+// x 128 23.3 -> 24.2, 8192 x 8192 44.0 -> 45.2; the residual forward at
+// 16384 x 4096 84.1 -> 88.1).
 #ifndef RMS_FWD_NT_LOAD
-#define RMS_FWD_NT_LOAD 0
+#define RMS_FWD_NT_LOAD 1
 #endif
 #ifndef RMS_FWD_NT_STORE
 #define RMS_FWD_NT_STORE 1
@@ -69,7 +71,9 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
     constexpr bool kNtLoad = RES ? RMS_RESFWD_NT_LOAD != 0 : RMS_FWD_NT_LOAD != 0;
     constexpr bool kNtStore = RES ? RMS_RESFWD_NT_STORE != 0 : RMS_FWD_NT_STORE != 0;
     constexpr int kDepth = kPrefetch ? RMS_FWD_PREFETCH : 0;
-    __shared__ double red[TEAM > kWave ? R * NWT : 1];
+    // Row-sum slots: two sets used by alternate row blocks (one barrier per
+    // sum; a set is rewritten only after the barrier of the block between).
+    __shared__ double red[TEAM > kWave ? 2 * R * NWT : 1];
 
     const int tid = threadIdx.x;
     const int team = tid / TEAM;
@@ -128,6 +132,7 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
             if (b < nrb) load_row(b, ahead[d]);
         }
     }
+    int set = 0;  // row-sum slot set of this block
     while (rb < nrb) {
         const int64_t nb = rb + gridDim.x;
         if constexpr (kDepth > 0) {
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
 #pragma unroll
             for (int k = 0; k < VEC; ++k) ss += sq64(v[c][k], (T*)nullptr);
         }
-        ss = team_sum<TEAM>(ss, red);
+        ss = team_sum_alt<TEAM>(ss, red + (TEAM > kWave ? set * R * NWT : 0));
         const double r = rsqrt_f64(ss * inv_h + (double)eps);
         const float rf = (float)r;
         if (active && lt == 0 && rstd) rstd[row] = rf;
@@ -183,6 +188,7 @@ __global__ __launch_bounds__(WG) void fwd_kernel(const T* x, const T* res, const
             for (int d = 0; d + 1 < kDepth; ++d) ahead[d] = ahead[d + 1];
         }
         rb = nb;
+        set ^= 1;
     }
 }
 
@@ -224,6 +230,7 @@ static hipError_t dispatch(const FwdArgs& a, bool residual, hipStream_t s) {
         g.team = 512;
         g.nch = 4;
     }
+
 #define RMS_CASE(TM, NC) \
     if (g.team == TM && g.nch == NC) return launch_cfg<T, VEC, TM, NC>(a, residual, s);
     RMS_CASE(1, 1) RMS_CASE(2, 1) RMS_CASE(4, 1) RMS_CASE(8, 1) RMS_CASE(16, 1) RMS_CASE(32, 1)

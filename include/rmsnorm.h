@@ -37,7 +37,11 @@
  *     128-bit load/store path (otherwise a scalar path of the same kernels).
  *   - Arithmetic: inputs are widened to fp32; the per-row sums (sum of
  *     squares, c) accumulate in fp64; each output is rounded once to its
- *     dtype (round to nearest even).  dw accumulates in fp32.
+ *     dtype (round to nearest even).  dw accumulates in fp32.  Squares are
+ *     formed in fp64 (exact for any finite input).  For bf16 I/O the
+ *     backward's products w*dy*x are formed in fp32, where they are exact
+ *     while 2^-126 <= |w*dy*x| < 2^128; the outputs themselves must be
+ *     representable in the I/O dtype.
  *   - Reductions run in a fixed order and no float atomics are used: for a
  *     given shape, dtype and library build, results are bitwise identical
  *     from run to run.

@@ -652,3 +652,40 @@ def test_scalar_path_width_limit():
     torch.cuda.synchronize()
     yo, _ = oracle.rmsnorm_fwd(synth.to_f64(xa, synth.BF16), synth.to_f64(wa, synth.BF16), wl.eps)
     assert_output("y", f64(y), yo, synth.BF16)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("scale_exp", [-70, 70, 100])
+@pytest.mark.parametrize("H", [128, 896, 4096, 8192])
+def test_extreme_magnitudes(dtype, scale_exp, H):
+    """Rows of x ~ N(0,1) * 2^k with k = -70, 70, 100 at eps = 0: squares and
+    w*dy*x products far outside fp32's range of exact products are formed in
+    fp64, so y, rstd, dx and dw still match the oracle to the usual bars (a
+    product formed in fp32 would overflow to inf, giving NaN, at 2^70 and
+    lose bits to underflow at 2^-70)."""
+    rows = 9
+    wl, x, w, dy, *_ = _inputs(rows, H, dtype, seed=H + 100 + scale_exp)
+    x = synth.quantise((synth.to_f64(x, dtype) * 2.0 ** scale_exp).astype(np.float32), dtype)
+    x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
+    assert np.all(np.isfinite(x64)) and np.max(np.abs(x64)) > 0
+    eps = 0.0
+    yo, ro = oracle.rmsnorm_fwd(x64, w64, eps)
+    r32, r32_d = oracle_stat(ro)
+    xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
+    y, rstd = _empty(rows, H, dtype), torch.full((rows,), float("nan"), device=DEV)
+    dx = _empty(rows, H, dtype)
+    dw = torch.full((H,), float("nan"), dtype=torch_dtype(dtype), device=DEV)
+    dxq = _empty(rows, H, dtype)
+    dwq = torch.full((H,), float("nan"), dtype=torch_dtype(dtype), device=DEV)
+    B.rmsnorm_fwd(xd, wd, y, rstd, eps)
+    B.rmsnorm_bwd(dyd, xd, wd, r32_d, None, dx, dw, _ws(rows, H, dtype), eps)
+    B.rmsnorm_bwd(dyd, xd, wd, None, None, dxq, dwq, _ws(rows, H, dtype), eps)
+    torch.cuda.synchronize()
+    assert_output("y", f64(y), yo, dtype)
+    assert_rstd_rounded(f64(rstd), ro)
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, eps, rstd=r32)
+    assert_output("dx", f64(dx), dxo, dtype)
+    assert_dw(f64(dw), dwo, dtype)
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, eps, rstd=None)
+    assert_output("dx (recompute)", f64(dxq), dxo, dtype)
+    assert_dw(f64(dwq), dwo, dtype)
