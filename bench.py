@@ -259,11 +259,15 @@ def kernel_names(C, calls):
 def bench_step(steps, warmup, burst_min=200):
     """The headline step on the bf16 residual 16384 x 4096 workload.
 
-    First each kernel of the step alone: max(steps, burst_min) back-to-back
+    First the step's kernels in bursts: max(steps, burst_min) back-to-back
     launches over the rotating buffer sets, bracketed by HIP events recorded
-    on the stream the kernels run on; the average per launch is the kernel's
-    duration plus the small dispatch gap between launches (this also brings
-    the GPU to its working clocks before the timed steps).  Then `warmup`
+    on the stream the kernels run on -- the forward alone, the backward row
+    pass alone, and the row pass followed by its dw reduce; the average per
+    launch is the kernel's duration plus the small dispatch gap between
+    launches, and the dw reduce is timed as what it adds to its row pass (a
+    burst of the reduce alone would time the host's launch rate, its kernel
+    being a few µs).  This also brings the GPU to its working clocks before
+    the timed steps.  Then `warmup`
     untimed steps and `steps` timed steps (residual forward, backward row
     pass with the residual-stream gradient, dw reduce) back to back,
     bracketed by synchronisation, with nothing else enqueued between the
@@ -284,18 +288,20 @@ def bench_step(steps, warmup, burst_min=200):
 
     def burst(idx):
         for i in range(sets.k):
-            run(plan[i][idx])
+            for j in idx:
+                run(plan[i][j])
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record(stream)
         for i in range(nb):
-            run(plan[i % sets.k][idx])
+            for j in idx:
+                run(plan[i % sets.k][j])
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / nb
 
-    per_kernel = [burst(j) for j in range(len(plan[0]))]
+    fwd_us, rows_us, bwd_us = burst((0,)), burst((1,)), burst((1, 2))
 
     for i in range(warmup):
         for c in plan[i % sets.k]:
@@ -320,7 +326,7 @@ def bench_step(steps, warmup, burst_min=200):
     return {
         "wl": wl, "k": sets.k, "ms_step": ms_step, "span_ms": span_ms, "names": names,
         "burst": nb,
-        "fwd_us": per_kernel[0], "rows_us": per_kernel[1], "reduce_us": per_kernel[2],
+        "fwd_us": fwd_us, "rows_us": rows_us, "bwd_us": bwd_us, "reduce_us": bwd_us - rows_us,
         "fwd_bytes": fwd_bytes(wl.rows, wl.H, e, residual=True),
         "bwd_bytes": bwd_bytes(wl.rows, wl.H, e, dres=True),
         "rows_bytes": bwd_rows_bytes(wl.rows, wl.H, e, dres=True),
@@ -831,43 +837,87 @@ def suite(path, reps=30, warmup=20):
 COUNTER_WORKLOADS = ["c1_f32_64x896", "c2_bf16_4096x4096", "c5a_bf16_262144x128",
                      "c5b_bf16_8192x8192", "c4_bf16_residual_16384x4096",
                      "wide_bf16_2048x32768", "wide_bf16_1024x65536",
-                     "wide_bf16_residual_2048x32768", "c3_bf16_decode_1x896"]
+                     "wide_bf16_residual_2048x32768", "c3_bf16_decode_1x896",
+                     "q_proj_bf16_1024x896"]
 
 
-def counters_pass(n):
+def counters_pass(n, plan_out=None):
     """Every workload's kernels, n launches each on rotating buffer sets, with
-    no timing: the program that rocprofv3 counter passes run over.  Per
-    workload, in COUNTER_WORKLOADS order, each repetition launches forward,
-    backward row pass and dw reduce (residual forward and the row pass with
-    dres for the residual workload; the one-row forward and the split-row
-    forward with 4 splits for decode), so every dw reduce dispatch follows the
-    row pass of its own workload."""
+    no timing: the program that rocprofv3 trace and counter passes run over.
+    Per workload, in COUNTER_WORKLOADS order: n forwards back to back, then n
+    times the backward row pass followed by its dw reduce (residual forward
+    and the row pass with dres for the residual workload) -- the bursts the
+    per-kernel timings of this file measure; decode runs n one-row forwards,
+    then n split-row forwards for each of 1, 4, 8 and 16 splits; the decode
+    projection n calls per split count.  plan_out, if given, receives the
+    launch plan as JSON: per workload, the kernels (named by the library's dry
+    run) in launch order, so that a trace can be cut into workloads."""
     import torch
-    from bwd_rmsnorm_fwd_amd import synth
 
     stream = torch.cuda.current_stream()
+    plan = []
     for name in COUNTER_WORKLOADS:
+        if name.startswith("q_proj"):
+            plan += gemv_pass(name, n, stream)
+            continue
         wl = workload_by_name(name)
         residual = wl.residual
         sets = Sets(wl, k=1 if wl.rows == 1 else None, residual=residual, dres=residual)
         C = Calls(sets, stream)
-        partials = torch.empty(4, dtype=torch.float32, device="cuda")
-        for i in range(n):
-            s = sets.sets[i % sets.k]
-            if wl.rows == 1:
-                run(C.fwd(s))
-                run(C.splitrow(s, partials, 4))
-            elif residual:
-                run(C.residual_fwd(s))
-                run(C.bwd_rows(s, x_key="h", dres=True))
-                run(C.dw_reduce(s))
-            else:
-                run(C.fwd(s))
-                run(C.bwd_rows(s))
-                run(C.dw_reduce(s))
+        if wl.rows == 1:
+            groups = [("fwd", [C.fwd(s) for s in sets.sets])]
+            for S in (1, 4, 8, 16):
+                parts = torch.empty(S, dtype=torch.float32, device="cuda")
+                groups.append((f"splitrow_S{S}", [C.splitrow(s, parts, S) for s in sets.sets]))
+            for label, calls in groups:
+                for i in range(n):
+                    run(calls[i % len(calls)])
+                plan.append({"workload": name, "op": label, "repeats": n,
+                             "kernels": [k for ks in kernel_names(C, calls[:1]) for k in ks]})
+        else:
+            seq = step_plan(C, sets, residual=residual)
+            meta = {"rows": wl.rows, "H": wl.H, "dtype": wl.dtype, "residual": residual,
+                    "cold_sets": sets.k}
+            for label, idx in (("fwd", (0,)), ("bwd_rows+dw_reduce", (1, 2))):
+                for i in range(n):
+                    for j in idx:
+                        run(seq[i % sets.k][j])
+                plan.append(dict(meta, workload=name, op=label, repeats=n,
+                                 kernels=[k for ks in kernel_names(C, [seq[0][j] for j in idx])
+                                          for k in ks]))
         torch.cuda.synchronize()
         del sets, C
         torch.cuda.empty_cache()
+    if plan_out:
+        with open(plan_out, "w") as f:
+            json.dump(plan, f, indent=1)
+
+
+def gemv_pass(name, n, stream):
+    """The split-K decode projection, n calls for each split count; returns
+    its part of the launch plan."""
+    import numpy as np
+    import torch
+    from bwd_rmsnorm_fwd_amd import binding as B
+    from bwd_rmsnorm_fwd_amd import synth
+    gw = synth.GEMV_WORKLOADS[name]
+    A = torch.from_numpy(gw.A().view(np.int16)).view(torch.bfloat16).cuda()
+    xv = torch.from_numpy(gw.x().view(np.int16)).view(torch.bfloat16).cuda()
+    yv = torch.empty(gw.N, dtype=torch.bfloat16, device="cuda")
+    L = B.lib()
+    plan = []
+    for splits in gw.splits:
+        parts = torch.empty(max(B.decode_gemv_partials_count(gw.N, splits), 1), device="cuda")
+        call = (L.decode_gemv_splitk,
+                (ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(xv.data_ptr()),
+                 ctypes.c_void_p(yv.data_ptr()), ctypes.c_void_p(parts.data_ptr()), parts.numel(),
+                 gw.N, gw.K, splits, B.BF16, ctypes.c_void_p(stream.cuda_stream)))
+        for _ in range(n):
+            run(call)
+        plan.append({"workload": name, "op": f"gemv_S{splits}", "repeats": n,
+                     "kernels": [l.split(" grid=")[0] for l in B.launches_of(call[0], *call[1])]})
+    torch.cuda.synchronize()
+    return plan
 
 
 # ---------------------------------------------------------------- entry
@@ -891,6 +941,8 @@ def main():
     ap.add_argument("--counters-pass", type=int, default=0, metavar="N",
                     help="instead of timing, launch every workload's kernels N times each "
                          "(the program for rocprofv3 counter passes), then the --copy-ref-mb copy")
+    ap.add_argument("--plan-out", default=None,
+                    help="with --counters-pass: write the launch plan (JSON) to this file")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -903,7 +955,7 @@ def main():
     import torch
     torch.cuda.init()
     if args.counters_pass:
-        counters_pass(args.counters_pass)
+        counters_pass(args.counters_pass, args.plan_out)
         copy_ref(args.copy_ref_mb)
         print(json.dumps({"counters_pass": args.counters_pass, "workloads": COUNTER_WORKLOADS,
                           "copy_ref_bytes": args.copy_ref_mb << 20}), flush=True)
@@ -942,16 +994,17 @@ def main():
                    "bytes_per_step": total_bytes},
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "fwd_us": round(r["fwd_us"], 3),
-        "bwd_us": round(r["rows_us"] + r["reduce_us"], 3),
+        "bwd_us": round(r["bwd_us"], 3),
         "bwd_rows_us": round(r["rows_us"], 3),
         "dw_reduce_us": round(r["reduce_us"], 3),
         "fwd_pct_peak": _pct(r["fwd_bytes"], r["fwd_us"])[1],
-        "bwd_pct_peak": _pct(r["bwd_bytes"], r["rows_us"] + r["reduce_us"])[1],
+        "bwd_pct_peak": _pct(r["bwd_bytes"], r["bwd_us"])[1],
         "event_span_ms_per_step": round(r["span_ms"], 5),
         "kernels": [k for ks in r["names"] for k in ks],
         "timing": f"value/ms_per_step: wall clock over the timed steps (no per-kernel events); "
                   f"per-kernel µs: HIP events around a burst of {r['burst']} back-to-back "
-                  f"launches of that kernel alone, run before the warm-up steps",
+                  f"launches (fwd alone, bwd row pass alone, row pass + dw reduce), run before "
+                  f"the warm-up steps; dw_reduce_us = bwd_us - bwd_rows_us",
         "roofline": {
             "kernel": dom_name,
             "bound": "hbm",
