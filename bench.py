@@ -968,7 +968,9 @@ def main():
     total_bytes = r["fwd_bytes"] + r["bwd_bytes"]
     value = total_bytes / (r["ms_step"] * 1e-3) / 1e9
     # The dominant kernel: the longer of the residual forward and the
-    # backward row pass inside the step.
+    # backward row pass, each timed in its burst (event pairs around single
+    # launches inside the steps were tried: the events themselves slowed the
+    # kernel they bracketed by up to 6%, by the trace of the same run).
     if r["fwd_us"] >= r["rows_us"]:
         dom_name, dom_us, dom_bytes = r["names"][0][0], r["fwd_us"], r["fwd_bytes"]
     else:
