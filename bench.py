@@ -264,10 +264,10 @@ def bench_step(steps, warmup, burst_min=200):
     on the stream the kernels run on -- the forward alone, the backward row
     pass alone, and the row pass followed by its dw reduce; the average per
     launch is the kernel's duration plus the small dispatch gap between
-    launches, and the dw reduce is timed as what it adds to its row pass (a
-    burst of the reduce alone would time the host's launch rate, its kernel
-    being a few µs).  This also brings the GPU to its working clocks before
-    the timed steps.  Then `warmup`
+    launches (the dw reduce is timed only with its row pass: a burst of the
+    reduce alone would time the host's launch rate, its kernel being a few
+    µs).  This also brings the GPU to its working clocks before the timed
+    steps.  Then `warmup`
     untimed steps and `steps` timed steps (residual forward, backward row
     pass with the residual-stream gradient, dw reduce) back to back,
     bracketed by synchronisation, with nothing else enqueued between the
@@ -326,7 +326,7 @@ def bench_step(steps, warmup, burst_min=200):
     return {
         "wl": wl, "k": sets.k, "ms_step": ms_step, "span_ms": span_ms, "names": names,
         "burst": nb,
-        "fwd_us": fwd_us, "rows_us": rows_us, "bwd_us": bwd_us, "reduce_us": bwd_us - rows_us,
+        "fwd_us": fwd_us, "rows_us": rows_us, "bwd_us": bwd_us,
         "fwd_bytes": fwd_bytes(wl.rows, wl.H, e, residual=True),
         "bwd_bytes": bwd_bytes(wl.rows, wl.H, e, dres=True),
         "rows_bytes": bwd_rows_bytes(wl.rows, wl.H, e, dres=True),
@@ -998,7 +998,6 @@ def main():
         "fwd_us": round(r["fwd_us"], 3),
         "bwd_us": round(r["bwd_us"], 3),
         "bwd_rows_us": round(r["rows_us"], 3),
-        "dw_reduce_us": round(r["reduce_us"], 3),
         "fwd_pct_peak": _pct(r["fwd_bytes"], r["fwd_us"])[1],
         "bwd_pct_peak": _pct(r["bwd_bytes"], r["bwd_us"])[1],
         "event_span_ms_per_step": round(r["span_ms"], 5),
@@ -1006,7 +1005,7 @@ def main():
         "timing": f"value/ms_per_step: wall clock over the timed steps (no per-kernel events); "
                   f"per-kernel µs: HIP events around a burst of {r['burst']} back-to-back "
                   f"launches (fwd alone, bwd row pass alone, row pass + dw reduce), run before "
-                  f"the warm-up steps; dw_reduce_us = bwd_us - bwd_rows_us",
+                  f"the warm-up steps",
         "roofline": {
             "kernel": dom_name,
             "bound": "hbm",
