@@ -81,6 +81,13 @@ def kernel_source_hash():
 
 # ---------------------------------------------------------------- device plumbing
 
+def cold_sets(rows, H, e, residual=False):
+    """Buffer sets to rotate so that the other sets' forwards read at least
+    COLD_BYTES between two uses of one set (at least 2, at most MAX_SETS)."""
+    read = rows * H * e * (2 if residual else 1)
+    return min(MAX_SETS, max(2, math.ceil(COLD_BYTES / read) + 1))
+
+
 class Sets:
     """K rotating buffer sets of one workload, filled with its seeded inputs.
     K is chosen so that between two uses of one set the other sets' calls of
@@ -109,8 +116,7 @@ class Sets:
         res = dev(wl.res()) if residual else None
         dres_t = dev(wl.dres()) if dres else None
         ws_bytes = max(B.rmsnorm_bwd_workspace_bytes(rows, H, self.code), 16)
-        read = rows * H * self.e * (2 if residual else 1)
-        self.k = k or min(MAX_SETS, max(2, math.ceil(COLD_BYTES / read) + 1))
+        self.k = k or cold_sets(rows, H, self.e, residual)
         self.sets = []
         for _ in range(self.k):
             s = {

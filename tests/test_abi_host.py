@@ -260,3 +260,19 @@ def test_bench_byte_formulas():
     assert bench.fwd_bytes(262144, 128, 2) == 135_266_560
     assert bench.bwd_bytes(8192, 8192, 2) == 402_718_720
     assert bench.fwd_bytes(64, 896, 4) == 462_592
+
+
+def test_bench_cold_rotation():
+    """The number of rotating buffer sets per workload: the other sets'
+    forwards read at least 2.5 x the 256 MB Infinity Cache in between."""
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.cold_sets(16384, 4096, 2, residual=True) == 4
+    assert bench.cold_sets(8192, 8192, 2) == 6
+    assert bench.cold_sets(262144, 128, 2) == 11
+    assert bench.cold_sets(4096, 4096, 2) == 21
+    assert bench.cold_sets(64, 896, 4) == bench.MAX_SETS
+    for rows, H, e, res in ((16384, 4096, 2, True), (8192, 8192, 2, False), (4096, 4096, 2, False)):
+        k = bench.cold_sets(rows, H, e, res)
+        read = rows * H * e * (2 if res else 1)
+        assert (k - 1) * read >= bench.COLD_BYTES > (k - 2) * read
