@@ -236,6 +236,56 @@ def test_degenerate_rows(dtype, H):
     assert_dw(f64(dw), dwo, dtype)
 
 
+def _same_nonfinite(name, g, o):
+    """g and o are NaN at the same places and equal (0 == -0) elsewhere."""
+    assert np.array_equal(np.isnan(g), np.isnan(o)), f"{name}: NaN pattern differs from the oracle"
+    fin = ~np.isnan(o)
+    assert np.array_equal(g[fin], o[fin]), f"{name}: non-NaN values differ from the oracle"
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("H", [128, 896, 4096, 8192, 16384, 32768])
+@pytest.mark.parametrize("saved", [True, False])
+def test_nonfinite_inputs_stay_in_their_row(dtype, H, saved):
+    """Rows are independent (P1 §4.1, §5.3), so a NaN or an infinity in x
+    reaches only its own row of y, rstd and dx, with what the double-precision
+    definition gives there: a NaN row is NaN throughout; a row holding one
+    infinity has mean(x^2) = inf, so r = 0, y = w x r is 0 except NaN where x
+    is infinite, and dx = r (w dy - x r^2 c) is NaN.  dw sums over every row,
+    so it is NaN in every column.  Every finite row is checked as usual."""
+    rows = 7
+    wl, x, w, dy, *_ = _inputs(rows, H, dtype, seed=H + 17)
+    x = synth.to_f64(x, dtype).astype(np.float32)
+    x[1, H // 2] = np.nan
+    x[3, H - 1] = np.inf
+    x[5, 0] = -np.inf
+    x = synth.quantise(x, dtype)
+    bad, good = [1, 3, 5], [0, 2, 4, 6]
+    eps = wl.eps
+    x64, w64, dy64 = (synth.to_f64(a, dtype) for a in (x, w, dy))
+    xd, wd, dyd = to_dev(x, dtype), to_dev(w, dtype), to_dev(dy, dtype)
+    y, rstd = _empty(rows, H, dtype), torch.empty(rows, device=DEV)
+    dx = _empty(rows, H, dtype)
+    dw = torch.zeros(H, dtype=torch_dtype(dtype), device=DEV)
+    yo, ro = oracle.rmsnorm_fwd(x64, w64, eps)
+    r32, r32_d = oracle_stat(ro)
+    B.rmsnorm_fwd(xd, wd, y, rstd, eps)
+    B.rmsnorm_bwd(dyd, xd, wd, r32_d if saved else None, None, dx, dw, _ws(rows, H, dtype), eps)
+    torch.cuda.synchronize()
+    yg, rg, dxg, dwg = f64(y), f64(rstd), f64(dx), f64(dw)
+    dxo, dwo = oracle.rmsnorm_bwd(dy64, x64, w64, eps, rstd=r32 if saved else None)
+    assert np.isnan(ro[1]) and ro[3] == 0.0 and ro[5] == 0.0, "oracle: r of the NaN and inf rows"
+    assert np.isnan(rg[1]) and rg[3] == 0.0 and rg[5] == 0.0, f"rstd of the non-finite rows: {rg[bad]}"
+    for i in bad:
+        _same_nonfinite(f"y row {i}", yg[i], yo[i])
+        _same_nonfinite(f"dx row {i}", dxg[i], dxo[i])
+        assert np.isnan(dxg[i]).all(), f"dx row {i} should be NaN throughout"
+    assert np.isnan(dwo).all() and np.isnan(dwg).all(), "dw should be NaN in every column"
+    assert_output("y", yg[good], yo[good], dtype)
+    assert_rstd_rounded(rg[good], ro[good])
+    assert_output("dx", dxg[good], dxo[good], dtype)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("H", [1, 7, 896, 4096])
 def test_constant_rows_eps0_give_signed_w(dtype, H):
