@@ -136,9 +136,19 @@ constexpr size_t kScratchBytes = RMSNORM_NOALLOC_SCRATCH_BYTES;
 constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_dev[kMaxDevices];
 
-rmsnorm_status_t scratch_address(void** out) {
+// The scratch of the current device, on which `stream` must run (the kernels
+// would otherwise address another GPU's copy).
+rmsnorm_status_t scratch_address(hipStream_t stream, void** out) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RMSNORM_ELAUNCH;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+            (void)hipGetLastError();
+            return RMSNORM_EINVAL;
+        }
+        if (sdev != dev) return RMSNORM_EINVAL;
+    }
     void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
     if (!p) {
         // With `dev` current: its own copy of the array.
@@ -300,7 +310,7 @@ rmsnorm_status_t rmsnorm_bwd_noalloc(const void* dy, const void* x, const void* 
         if (rms::dry_run_active()) {
             ws = reinterpret_cast<void*>(uintptr_t{256});  // nothing is launched
         } else {
-            st = scratch_address(&ws);
+            st = scratch_address(stream, &ws);
             if (st != RMSNORM_OK) return st;
         }
     }

@@ -175,7 +175,9 @@ rmsnorm_status_t rmsnorm_bwd_dw_reduce(const void *workspace, size_t workspace_b
  *   Arguments as for rmsnorm_bwd, without workspace/workspace_bytes.
  *   Returns RMSNORM_ESCRATCH, enqueuing nothing, when
  *   rmsnorm_bwd_workspace_bytes(rows, H, dtype) > RMSNORM_NOALLOC_SCRATCH_BYTES,
- *   and RMSNORM_ELAUNCH if HIP cannot give the scratch's device address.
+ *   RMSNORM_EINVAL when `stream` belongs to a device other than the current
+ *   one (the scratch used is the current device's), and RMSNORM_ELAUNCH if
+ *   HIP cannot give the scratch's device address.
  * No allocation of any kind: the scratch's address on the current device is
  * looked up once (hipGetSymbolAddress) on that device's first call.  Every
  * call on a GPU shares that GPU's one scratch array (the row pass overwrites

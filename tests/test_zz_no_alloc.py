@@ -3,7 +3,8 @@ called through the C ABI, against rmsnorm_bwd on the same inputs: dx and dw
 must be bitwise equal (same kernels, same reduction order), on two calls in
 a row, the second with a smaller input that reuses the same scratch; plus a
 third call on the oracle's inputs against the oracle, and the refusal of a
-shape that needs more scratch than the library holds."""
+shape that needs more scratch than the library holds, and the call recorded
+under HIP graph capture."""
 import ctypes
 
 import numpy as np
@@ -30,11 +31,13 @@ def _case(rows, H, dtype, seed, dres):
     return d
 
 
-def _noalloc(c, dtype):
+def _noalloc(c, dtype, out=None):
     rows, H = c["xd"].shape
     td = torch_dtype(dtype)
-    dx = torch.full((rows, H), float("nan"), dtype=td, device=DEV)
-    dw = torch.full((H,), float("nan"), dtype=td, device=DEV)
+    if out is None:
+        out = (torch.full((rows, H), float("nan"), dtype=td, device=DEV),
+               torch.full((H,), float("nan"), dtype=td, device=DEV))
+    dx, dw = out
     L = B.lib()
     p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     st = L.rmsnorm_bwd_noalloc(p(c["dyd"]), p(c["xd"]), p(c["wd"]), p(c["rstd"]), p(c["dresd"]),
@@ -105,3 +108,34 @@ def test_noalloc_recompute_and_refusal():
     finally:
         B.rmsnorm_set_dry_run(False)
     assert st == B.ESCRATCH, B.status_str(st)
+
+
+def test_noalloc_in_a_captured_graph():
+    """Recorded under HIP graph capture (one of the callers the entry point is
+    for), the call replays to the eager call's dx and dw bit for bit, also
+    when an eager call of another shape has used the scratch in between."""
+    dtype = synth.BF16
+    c = _case(2048, 4096, dtype, seed=61, dres=True)
+    other = _case(300, 896, dtype, seed=62, dres=False)
+    dx_e, dw_e = _noalloc(c, dtype)
+    torch.cuda.synchronize()
+    rows, H = c["xd"].shape
+    td = torch_dtype(dtype)
+    dx = torch.empty((rows, H), dtype=td, device=DEV)
+    dw = torch.empty((H,), dtype=td, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            _noalloc(c, dtype, out=(dx, dw))
+    torch.cuda.current_stream().wait_stream(s)
+    for k in range(3):
+        dx.fill_(float("nan"))
+        dw.fill_(float("nan"))
+        _noalloc(other, dtype)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(dx), _bits(dx_e)), (k, "dx")
+        assert torch.equal(_bits(dw), _bits(dw_e)), (k, "dw")
