@@ -13,10 +13,14 @@ Prints one JSON line.  `value` is achieved HBM GB/s over the whole step,
 counting the algorithmic bytes only (residual fwd: x, res, w read, h, y,
 rstd written; bwd: dy, dres, h, w, rstd read, dh, dw written), by wall clock
 over the timed steps.  `roofline` is for the step's dominant kernel, timed
-with HIP events around each of its launches inside the steps, on the stream
-it runs on; its name comes from the library's dry-run report.  `configs`
-gives fwd and bwd µs / GB/s / % of 8 TB/s for every other configuration and
-µs per call for decode (plain, C loop, HIP graph) and the split-K q_proj.
+with HIP events around a burst of its back-to-back launches before the
+steps, on the stream it runs on; its name comes from the library's dry-run
+report.  `stream_ceiling` times plain streams of the same reads and writes
+(bench_stream.hip: loads and stores only) on the same cold rotation, so each
+kernel can be set against what merely moving its bytes takes.  `configs`
+gives fwd and bwd µs (median and P95) / GB/s / % of 8 TB/s for every other
+configuration, with its stream ceilings and a warm-buffer figure (not HBM),
+and µs per call for decode (plain, C loop, HIP graph) and the split-K q_proj.
 `cpu_baseline` times the double-precision oracle on the host, on one thread
 and on all the cores this process may use.
 
@@ -201,6 +205,53 @@ def c_loops():
     return L
 
 
+def stream_lib():
+    """The plain-stream kernels (bwd_rmsnorm_fwd_amd/bench_stream.hip), or
+    None when they have not been built."""
+    path = os.path.join(ROOT, "bwd_rmsnorm_fwd_amd", "libbench_stream.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.bench_stream.argtypes = [i32, i32, vp, vp, vp, vp, vp, i64, vp]
+    L.bench_stream.restype = i32
+    return L
+
+
+# Row tensors read and written by each kernel (w and rstd aside).
+STREAM_PATTERN = {"fwd": (1, 1), "residual_fwd": (2, 2), "bwd_rows": (2, 1), "bwd_rows_dres": (3, 1)}
+
+
+def stream_ceiling(SL, nr, nw, nbytes, stream, reps=10, burst=16):
+    """A plain stream of `nr` reads and `nw` writes of `nbytes` each (rounded
+    down to whole 8 KB blocks), timed like the configurations: `reps` bursts
+    of `burst` launches over buffer sets rotating so that the other sets read
+    at least COLD_BYTES between two uses of one set; median µs, GB/s and % of
+    8 TB/s over the bytes moved."""
+    import torch
+    nbytes = nbytes // 8192 * 8192
+    if SL is None or nbytes == 0:
+        return None
+    k = min(MAX_SETS, max(2, math.ceil(COLD_BYTES / (nr * nbytes)) + 1))
+    bufs = [[torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nr + nw)]
+            for _ in range(k)]
+    st = ctypes.c_void_p(stream.cuda_stream)
+    calls = []
+    for b in bufs:
+        ptr = [ctypes.c_void_p(t.data_ptr()) for t in b]
+        ins = ptr[:nr] + [None] * (3 - nr)
+        outs = ptr[nr:] + [None] * (2 - nw)
+        calls.append(((SL.bench_stream, (nr, nw, *ins, *outs, nbytes, st)),))
+    (t,) = time_calls(calls, k, reps, 2 * k, stream, burst)
+    del bufs, calls
+    torch.cuda.empty_cache()
+    us = statistics.median(t)
+    gbs, pct = _pct((nr + nw) * nbytes, us)
+    plural = lambda n, w: f"{n} {w}{'s' if n > 1 else ''}"
+    return {"pattern": f"{plural(nr, 'read')} + {plural(nw, 'write')}", "bytes_per_stream": nbytes,
+            "buffer_sets": k, "us": round(us, 3), "GB_s": gbs, "pct_peak": pct}
+
+
 def time_c_loop(loop, call, ncalls, stream):
     """µs per call of `call` (fn, args) made `ncalls` times back to back by a
     loop in C (loop(fn, n, *args)), bracketed by events on `stream`."""
@@ -344,6 +395,25 @@ def _pct(nbytes, us):
     return round(gbs, 1), round(100 * gbs / PEAK_GBS, 2)
 
 
+def _p95(us):
+    v = sorted(us)
+    return round(v[min(len(v) - 1, int(0.95 * len(v)))], 3)
+
+
+def ceilings_of(wl, e, residual, fwd_gbs, rows_gbs, stream):
+    """The plain streams of a workload's forward and backward row pass (same
+    row tensors read and written, same size) and each kernel's GB/s as a
+    fraction of its stream's."""
+    SL = stream_lib()
+    nbytes = wl.rows * wl.H * e
+    cf = stream_ceiling(SL, *STREAM_PATTERN["residual_fwd" if residual else "fwd"], nbytes, stream)
+    cb = stream_ceiling(SL, *STREAM_PATTERN["bwd_rows_dres" if residual else "bwd_rows"], nbytes,
+                        stream)
+    return {"stream_ceiling": {"fwd": cf, "bwd_rows": cb},
+            "fwd_vs_stream": round(fwd_gbs / cf["GB_s"], 3) if cf else None,
+            "bwd_rows_vs_stream": round(rows_gbs / cb["GB_s"], 3) if cb else None}
+
+
 def config_table(reps=10, burst=16):
     """fwd / bwd µs per call (median of `reps` bursts of `burst` back-to-back
     launches on cold rotating buffers, events at the burst ends), GB/s and %
@@ -374,22 +444,30 @@ def config_table(reps=10, burst=16):
         tr, tb = time_calls(b_calls, sets.k, reps, 2 * sets.k, stream, burst)
         (ts,) = time_calls(step_plan(C, sets, residual=res), sets.k, reps, 2 * sets.k, stream,
                            burst)[2:]
+        # The same calls on one buffer set over and over (inputs partly or
+        # wholly in the Infinity Cache): context only, not an HBM figure.
+        (wf,) = time_calls(f_calls[:1], 1, reps, 2, stream, burst)
+        wr, wb = time_calls(b_calls[:1], 1, reps, 2, stream, burst)
         fb = fwd_bytes(wl.rows, wl.H, e, residual=res)
         bb = bwd_bytes(wl.rows, wl.H, e, dres=res)
         rb = bwd_rows_bytes(wl.rows, wl.H, e, dres=res)
+        med = lambda v: round(statistics.median(v), 3)
         d = {"rows": wl.rows, "H": wl.H, "dtype": wl.dtype, "residual": res,
-             "fwd_us": round(statistics.median(tf), 3), "bwd_rows_us": round(statistics.median(tr), 3),
-             "bwd_us": round(statistics.median(tb), 3), "step_us": round(statistics.median(ts), 3),
-             "fwd_bytes": fb, "bwd_bytes": bb}
+             "fwd_us": med(tf), "bwd_rows_us": med(tr), "bwd_us": med(tb), "step_us": med(ts),
+             "fwd_us_p95": _p95(tf), "bwd_rows_us_p95": _p95(tr), "bwd_us_p95": _p95(tb),
+             "step_us_p95": _p95(ts), "fwd_bytes": fb, "bwd_bytes": bb}
         d["fwd_GB_s"], d["fwd_pct_peak"] = _pct(fb, d["fwd_us"])
         d["bwd_rows_GB_s"], d["bwd_rows_pct_peak"] = _pct(rb, d["bwd_rows_us"])
         d["bwd_GB_s"], d["bwd_pct_peak"] = _pct(bb, d["bwd_us"])
         d["step_GB_s"], d["step_pct_peak"] = _pct(fb + bb, d["step_us"])
+        d["warm_same_buffers_not_hbm"] = {"fwd_us": med(wf), "bwd_rows_us": med(wr),
+                                          "bwd_us": med(wb)}
         d["kernels"] = sorted({k for ks in kernel_names(C, step_plan(C, sets, residual=res)[0])
                                for k in ks})
-        out[name] = d
         del sets, C
         torch.cuda.empty_cache()
+        d.update(ceilings_of(wl, e, res, d["fwd_GB_s"], d["bwd_rows_GB_s"], stream))
+        out[name] = d
 
     # Decode rows = 1, H = 896: the one-wavefront row kernel and the split-row
     # path with S = 1, 4, 8, 16, each 10,000 calls back to back on one stream.
@@ -1024,6 +1102,10 @@ def main():
             "avg_launch_us": round(dom_us, 3),
         },
     }
+    e = 4 if wl.dtype == "f32" else 2
+    ceil = ceilings_of(wl, e, True, _pct(r["fwd_bytes"], r["fwd_us"])[0],
+                       _pct(r["rows_bytes"], r["rows_us"])[0], torch.cuda.current_stream())
+    line.update(ceil)
     if configs is not None:
         line["configs"] = configs
     if not args.no_cpu_baseline:

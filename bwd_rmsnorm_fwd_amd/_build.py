@@ -54,6 +54,7 @@ def build(out_path: str = LIB_PATH, defines=(), build_dir: str | None = None, jo
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out_path)
     build_bench_loops()
+    build_bench_stream()
     return out_path
 
 
@@ -96,6 +97,21 @@ def build_bench_loops(out_path: str = BENCH_LOOPS_PATH) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for bench_loops.cpp:\n{' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, out_path)
+    return out_path
+
+
+BENCH_STREAM_SRC = os.path.join(PKG, "bench_stream.hip")
+BENCH_STREAM_PATH = os.path.join(PKG, "libbench_stream.so")
+
+
+def build_bench_stream(out_path: str = BENCH_STREAM_PATH) -> str:
+    """The benchmark's plain-stream kernels (the ceiling figures), gfx950."""
+    tmp = out_path + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", "-o", tmp, BENCH_STREAM_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for bench_stream.hip:\n{' '.join(cmd)}\n{r.stderr}")
     os.replace(tmp, out_path)
     return out_path
 

@@ -206,6 +206,25 @@ def _check_dispatch_of_workloads():
     assert st == B.EINVAL and d == []
 
 
+def _check_bench_stream_validation():
+    """The benchmark's plain-stream helper refuses arguments outside its
+    limits before any HIP call."""
+    sys.path.insert(0, ROOT)
+    import bench
+    SL = bench.stream_lib()
+    assert SL is not None, "libbench_stream.so is not built"
+    A = ctypes.c_void_p(0x10000)
+    f = SL.bench_stream
+    assert f(0, 1, A, None, None, A, None, 8192, None) == 1          # no read stream
+    assert f(4, 1, A, A, A, A, None, 8192, None) == 1                 # more than 3 reads
+    assert f(1, 3, A, None, None, A, A, 8192, None) == 1              # more than 2 writes
+    assert f(1, 1, A, None, None, A, None, 8191, None) == 1           # not whole 8 KB blocks
+    assert f(1, 1, A, None, None, A, None, 0, None) == 1
+    assert f(2, 1, A, None, None, A, None, 8192, None) == 1           # second read missing
+    assert f(1, 2, A, None, None, A, None, 8192, None) == 1           # second write missing
+    assert f(1, 1, MIS, None, None, A, None, 8192, None) == 1         # misaligned
+
+
 HIDDEN_ENV = {"HIP_VISIBLE_DEVICES": "-1", "ROCR_VISIBLE_DEVICES": "-1", "CUDA_VISIBLE_DEVICES": "-1"}
 
 CHILD = r"""
@@ -225,7 +244,8 @@ print("ok")
 
 @pytest.mark.parametrize("check", ["_check_fwd_validation", "_check_bwd_validation_and_workspace",
                                    "_check_splitrow_validation", "_check_gemv_validation",
-                                   "_check_dispatch_of_workloads"])
+                                   "_check_dispatch_of_workloads",
+                                   "_check_bench_stream_validation"])
 def test_validation_without_a_device(check):
     env = dict(os.environ, **HIDDEN_ENV)
     code = CHILD.format(tests=os.path.dirname(os.path.abspath(__file__)), root=ROOT, fn=check)
