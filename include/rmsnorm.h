@@ -42,6 +42,11 @@
  *     backward's products w*dy*x are formed in fp32, where they are exact
  *     while 2^-126 <= |w*dy*x| < 2^128; the outputs themselves must be
  *     representable in the I/O dtype.
+ *   - Non-finite inputs follow IEEE arithmetic of the definition within
+ *     their row: a NaN in a row of x makes that row's y, rstd and dx NaN; an
+ *     infinity gives r = 0 (y = 0, NaN where x is infinite; dx NaN).  dw sums
+ *     over rows, so it is then NaN in every column.  Other rows are
+ *     unaffected.
  *   - Reductions run in a fixed order and no float atomics are used: for a
  *     given shape, dtype and library build, results are bitwise identical
  *     from run to run.

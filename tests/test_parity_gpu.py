@@ -286,6 +286,46 @@ def test_nonfinite_inputs_stay_in_their_row(dtype, H, saved):
     assert_output("dx", dxg[good], dxo[good], dtype)
 
 
+def _bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("rows,H", [(37, 128), (9, 896), (300, 4096), (5, 8192), (3, 16384),
+                                    (2, 32768), (2, 65536), (1000, 77)])
+def test_documented_aliasing(rows, H, dtype):
+    """The aliasing the C header allows gives the same bits as separate
+    buffers: h written over x or over res in the residual forward (an
+    in-place residual update), and dx written over dy or over dres in the
+    backward, on every kind of row kernel (register tiles, LDS-staged,
+    row-in-LDS, streaming, scalar)."""
+    wl, x, w, dy, res, dres = _inputs(rows, H, dtype, seed=rows + H + 29)
+    xd, wd, dyd, rd, drd = (to_dev(a, dtype) for a in (x, w, dy, res, dres))
+    eps = wl.eps
+    h, y, rstd = _empty(rows, H, dtype), _empty(rows, H, dtype), torch.empty(rows, device=DEV)
+    B.rmsnorm_residual_fwd(xd, rd, wd, h, y, rstd, eps)
+    for over in ("x", "res"):
+        xa, ra = xd.clone(), rd.clone()
+        ya, ra_st = _empty(rows, H, dtype), torch.empty(rows, device=DEV)
+        ha = xa if over == "x" else ra
+        B.rmsnorm_residual_fwd(xa, ra, wd, ha, ya, ra_st, eps)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(ha), _bits(h)), f"h over {over}"
+        assert torch.equal(_bits(ya), _bits(y)) and torch.equal(ra_st, rstd), f"y, rstd (h over {over})"
+    dx, dw = _empty(rows, H, dtype), torch.empty(H, dtype=torch_dtype(dtype), device=DEV)
+    ws = _ws(rows, H, dtype)
+    for saved in (rstd, None):
+        B.rmsnorm_bwd(dyd, h, wd, saved, drd, dx, dw, ws, eps)
+        for over in ("dy", "dres"):
+            dya, dra = dyd.clone(), drd.clone()
+            dwa = torch.empty_like(dw)
+            dxa = dya if over == "dy" else dra
+            B.rmsnorm_bwd(dya, h, wd, saved, dra, dxa, dwa, ws, eps)
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(dxa), _bits(dx)), f"dx over {over} (rstd saved: {saved is not None})"
+            assert torch.equal(_bits(dwa), _bits(dw)), f"dw (dx over {over})"
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("H", [1, 7, 896, 4096])
 def test_constant_rows_eps0_give_signed_w(dtype, H):
