@@ -194,6 +194,15 @@ def _check_dispatch_of_workloads():
         assert st == B.OK and len(d) == 2, d
         assert d[0].startswith("rms::split_sumsq_kernel") and f"grid=1x{S}x1" in d[0], d
         assert d[1].startswith("rms::split_finalize_kernel") and "grid=1x1x1" in d[1], d
+    # q_proj GEMV 1024 x 896: one kernel unsplit; partials + splitk_reduce split.
+    for S in (1, 4, 8, 16):
+        n = L.decode_gemv_partials_count(1024, S)
+        st, g = _dry(L.decode_gemv_splitk, A, A, A, A if S > 1 else None, n, 1024, 896, S, B.BF16,
+                     None)
+        assert st == B.OK and len(g) == (1 if S == 1 else 2), g
+        assert g[0].startswith("rms::gemv_splitk_kernel<unsigned short,"), g
+        if S > 1:
+            assert g[1].startswith("rms::splitk_reduce_kernel<unsigned short>"), g
     # Wide rows: the LDS-staged, row-in-LDS and streaming backward kernels.
     assert "bwd_rows_staged_kernel" in bwd(2730, 12288, B.BF16)[1][0]
     assert "bwd_rows_ldsrow_kernel" in bwd(2048, 32768, B.BF16)[1][0]
