@@ -176,6 +176,13 @@ class Calls:
                  p(s["dx"]), p(s["ws"]), self.sets.ws_bytes, self.rows, self.H, self.eps, self.code,
                  self.stream))
 
+    def bwd(self, s):
+        p = self.p
+        return (self.L.rmsnorm_bwd,
+                (p(s["dy"]), p(s["x"]), p(s["w"]), p(s["rstd"]), None, p(s["dx"]), p(s["dw"]),
+                 p(s["ws"]), self.sets.ws_bytes, self.rows, self.H, self.eps, self.code,
+                 self.stream))
+
     def dw_reduce(self, s):
         p = self.p
         return (self.L.rmsnorm_bwd_dw_reduce,
@@ -200,7 +207,8 @@ def c_loops():
     L.bench_fwd_loop.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, f32, i32, vp]
     L.bench_splitrow_loop.argtypes = [vp, i32, vp, vp, vp, vp, vp, sz, i64, i64, f32, i32, i32, vp]
     L.bench_gemv_loop.argtypes = [vp, i32, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
-    for f in (L.bench_fwd_loop, L.bench_splitrow_loop, L.bench_gemv_loop):
+    L.bench_bwd_loop.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, f32, i32, vp]
+    for f in (L.bench_fwd_loop, L.bench_splitrow_loop, L.bench_gemv_loop, L.bench_bwd_loop):
         f.restype = i32
     return L
 
@@ -464,6 +472,17 @@ def config_table(reps=10, burst=16):
                                           "bwd_us": med(wb)}
         d["kernels"] = sorted({k for ks in kernel_names(C, step_plan(C, sets, residual=res)[0])
                                for k in ks})
+        if name == "c1_f32_64x896":
+            # Launch-bound: µs per call of the forward and of the whole
+            # backward, also from a loop in C and replayed from HIP graphs.
+            CL = c_loops()
+            s0 = sets.sets[0]
+            d["us_per_call"] = {
+                "fwd": time_decode(lambda st: Calls(sets, st).fwd(s0), stream,
+                                   CL.bench_fwd_loop if CL else None),
+                "bwd": time_decode(lambda st: Calls(sets, st).bwd(s0), stream,
+                                   CL.bench_bwd_loop if CL else None),
+                "calls": 10000}
         del sets, C
         torch.cuda.empty_cache()
         d.update(ceilings_of(wl, e, res, d["fwd_GB_s"], d["bwd_rows_GB_s"], stream))

@@ -14,6 +14,8 @@ typedef int (*fwd_fn)(const void*, const void*, void*, float*, int64_t, int64_t,
                       hipStream_t);
 typedef int (*splitrow_fn)(const void*, const void*, void*, float*, float*, size_t, int64_t,
                            int64_t, float, int, int, hipStream_t);
+typedef int (*bwd_fn)(const void*, const void*, const void*, const float*, const void*, void*,
+                      void*, void*, size_t, int64_t, int64_t, float, int, hipStream_t);
 typedef int (*gemv_fn)(const void*, const void*, void*, float*, size_t, int64_t, int64_t, int,
                        int, hipStream_t);
 
@@ -23,6 +25,17 @@ int bench_fwd_loop(void* fn, int n, const void* x, const void* w, void* y, float
     fwd_fn f = (fwd_fn)fn;
     for (int i = 0; i < n; ++i) {
         const int st = f(x, w, y, rstd, rows, H, eps, dtype, s);
+        if (st) return st;
+    }
+    return 0;
+}
+
+int bench_bwd_loop(void* fn, int n, const void* dy, const void* x, const void* w,
+                   const float* rstd, const void* dres, void* dx, void* dw, void* ws,
+                   size_t ws_bytes, int64_t rows, int64_t H, float eps, int dtype, hipStream_t s) {
+    bwd_fn f = (bwd_fn)fn;
+    for (int i = 0; i < n; ++i) {
+        const int st = f(dy, x, w, rstd, dres, dx, dw, ws, ws_bytes, rows, H, eps, dtype, s);
         if (st) return st;
     }
     return 0;
