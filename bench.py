@@ -1122,7 +1122,7 @@ def main():
         },
     }
     e = 4 if wl.dtype == "f32" else 2
-    ceil = ceilings_of(wl, e, True, _pct(r["fwd_bytes"], r["fwd_us"])[0],
+    ceil = ceilings_of(wl, e, wl.residual, _pct(r["fwd_bytes"], r["fwd_us"])[0],
                        _pct(r["rows_bytes"], r["rows_us"])[0], torch.cuda.current_stream())
     line.update(ceil)
     if configs is not None:
