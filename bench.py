@@ -230,7 +230,7 @@ def stream_lib():
 STREAM_PATTERN = {"fwd": (1, 1), "residual_fwd": (2, 2), "bwd_rows": (2, 1), "bwd_rows_dres": (3, 1)}
 
 
-def stream_ceiling(SL, nr, nw, nbytes, stream, reps=10, burst=16):
+def stream_ceiling(SL, nr, nw, nbytes, stream, reps=13, burst=16):
     """A plain stream of `nr` reads and `nw` writes of `nbytes` each (rounded
     down to whole 8 KB blocks), timed like the configurations: `reps` bursts
     of `burst` launches over buffer sets rotating so that the other sets read
@@ -422,7 +422,7 @@ def ceilings_of(wl, e, residual, fwd_gbs, rows_gbs, stream):
             "bwd_rows_vs_stream": round(rows_gbs / cb["GB_s"], 3) if cb else None}
 
 
-def config_table(reps=10, burst=16):
+def config_table(reps=13, burst=16):
     """fwd / bwd µs per call (median of `reps` bursts of `burst` back-to-back
     launches on cold rotating buffers, events at the burst ends), GB/s and %
     of 8 TB/s over the algorithmic bytes, for every configuration; decode as
