@@ -14,8 +14,8 @@ counting the algorithmic bytes only (residual fwd: x, res, w read, h, y,
 rstd written; bwd: dy, dres, h, w, rstd read, dh, dw written), by wall clock
 over the timed steps.  `roofline` is for the step's dominant kernel, timed
 with HIP events around a burst of its back-to-back launches before the
-steps, on the stream it runs on; its name comes from the library's dry-run
-report.  `stream_ceiling` times plain streams of the same reads and writes
+steps (the row pass also in a burst of row pass + dw reduce pairs), on the
+stream it runs on; its name comes from the library's dry-run report.  `stream_ceiling` times plain streams of the same reads and writes
 (bench_stream.hip: loads and stores only) on the same cold rotation, so each
 kernel can be set against what merely moving its bytes takes.  `configs`
 gives fwd and bwd µs (median and P95) / GB/s / % of 8 TB/s for every other
