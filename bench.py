@@ -398,6 +398,20 @@ def bench_step(steps, warmup, burst_min=200):
     }
 
 
+def pick_roofline(r):
+    """The dominant kernel of the headline step from its burst timings `r`
+    (fwd_us, rows_us: bursts of each alone; bwd_us: burst of row pass + dw
+    reduce pairs; names: kernel names per call; fwd_bytes, rows_bytes).  The
+    row pass's figure is the smaller of its two bursts, each an upper bound
+    on its duration.  Returns (name, µs, bytes, how it was timed, row-pass µs)."""
+    rows_us, rows_basis = r["rows_us"], "burst of itself"
+    if r["bwd_us"] < rows_us:
+        rows_us, rows_basis = r["bwd_us"], "burst of (row pass, dw reduce) pairs, the reduce included"
+    if r["fwd_us"] >= rows_us:
+        return r["names"][0][0], r["fwd_us"], r["fwd_bytes"], "burst of itself", rows_us
+    return r["names"][1][0], rows_us, r["rows_bytes"], rows_basis, rows_us
+
+
 def _pct(nbytes, us):
     gbs = nbytes / (us * 1e-6) / 1e9
     return round(gbs, 1), round(100 * gbs / PEAK_GBS, 2)
@@ -1079,15 +1093,7 @@ def main():
     # itself than between reduces or inside the steps, where traces put it
     # within 1% of the forward.  (Events around each launch would add their
     # own 5-6 µs per launch, by the trace of the same run.)
-    rows_us, rows_basis = r["rows_us"], "burst of itself"
-    if r["bwd_us"] < rows_us:
-        rows_us, rows_basis = r["bwd_us"], "burst of (row pass, dw reduce) pairs, the reduce included"
-    if r["fwd_us"] >= rows_us:
-        dom_name, dom_us, dom_bytes = r["names"][0][0], r["fwd_us"], r["fwd_bytes"]
-        basis = "burst of itself"
-    else:
-        dom_name, dom_us, dom_bytes = r["names"][1][0], rows_us, r["rows_bytes"]
-        basis = rows_basis
+    dom_name, dom_us, dom_bytes, basis, rows_us = pick_roofline(r)
     ach = dom_bytes / (dom_us * 1e-6) / 1e9
     line = {
         "metric": METRIC,

@@ -305,3 +305,22 @@ def test_bench_cold_rotation():
         k = bench.cold_sets(rows, H, e, res)
         read = rows * H * e * (2 if res else 1)
         assert (k - 1) * read >= bench.COLD_BYTES > (k - 2) * read
+
+
+def test_bench_roofline_choice():
+    """The roofline kernel is the longer of the forward and the row pass; the
+    row pass counts as the smaller of its own burst and its (row pass, dw
+    reduce) pair burst."""
+    sys.path.insert(0, ROOT)
+    import bench
+    base = {"names": [["fwd_k"], ["rows_k"], ["red_k"]], "fwd_bytes": 10, "rows_bytes": 20}
+    # Row pass slower alone than with its reduce: the pair's figure is used.
+    r = dict(base, fwd_us=86.0, rows_us=95.0, bwd_us=88.0)
+    assert bench.pick_roofline(r) == ("rows_k", 88.0, 20, "burst of (row pass, dw reduce) pairs, "
+                                      "the reduce included", 88.0)
+    # The row pass alone is the smaller figure and still longer than the forward.
+    r = dict(base, fwd_us=86.0, rows_us=87.0, bwd_us=89.5)
+    assert bench.pick_roofline(r)[:4] == ("rows_k", 87.0, 20, "burst of itself")
+    # The forward is the longer kernel.
+    r = dict(base, fwd_us=86.5, rows_us=86.2, bwd_us=88.9)
+    assert bench.pick_roofline(r) == ("fwd_k", 86.5, 10, "burst of itself", 86.2)
