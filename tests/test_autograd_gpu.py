@@ -53,16 +53,22 @@ def test_residual_autograd_both_streams():
     assert_dw(f64(w.grad), dwo, dtype)
 
 
-def test_gradcheck_page_shape_fp32():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_gradcheck_page_shape_fp32(seed):
     """P1 §5.6 runs gradcheck at x (2, 32), eps 1e-6.  The library has no
     fp64 I/O, so this is the fp32 version: the analytic backward against
-    central differences of the GPU forward, with fp32-sized steps and
-    tolerances."""
-    torch.manual_seed(0)
+    central differences of the GPU forward.  Tolerances follow from the
+    arithmetic: y is the fp32 rounding of an exact value, so a difference
+    quotient over 2h = 8e-3 carries about 6e-8 |y| / 4e-3 = 1.5e-5 of
+    rounding, and the h^2 truncation term is a few 1e-6 at these magnitudes
+    (the same differences of an fp64 forward rounded to fp32, on the host,
+    stay within 4e-5 + 1e-3 of the exact Jacobian for five seeds); a slip in
+    the backward of 1e-3 relative or more fails."""
+    torch.manual_seed(seed)
     x = torch.randn(2, 32, device=DEV, dtype=torch.float32, requires_grad=True)
     w = torch.randn(32, device=DEV, dtype=torch.float32, requires_grad=True)
-    assert torch.autograd.gradcheck(lambda a, b: rms_norm(a, b, 1e-6), (x, w), eps=1e-3,
-                                    atol=2e-2, rtol=2e-2, nondet_tol=0.0, fast_mode=False)
+    assert torch.autograd.gradcheck(lambda a, b: rms_norm(a, b, 1e-6), (x, w), eps=4e-3,
+                                    atol=2e-4, rtol=1e-3, nondet_tol=0.0, fast_mode=False)
 
 
 def test_module_and_no_double_backward():
