@@ -224,14 +224,15 @@ def _check_bench_stream_validation():
     assert SL is not None, "libbench_stream.so is not built"
     A = ctypes.c_void_p(0x10000)
     f = SL.bench_stream
-    assert f(0, 1, A, None, None, A, None, 8192, None) == 1          # no read stream
-    assert f(4, 1, A, A, A, A, None, 8192, None) == 1                 # more than 3 reads
-    assert f(1, 3, A, None, None, A, A, 8192, None) == 1              # more than 2 writes
-    assert f(1, 1, A, None, None, A, None, 8191, None) == 1           # not whole 8 KB blocks
-    assert f(1, 1, A, None, None, A, None, 0, None) == 1
-    assert f(2, 1, A, None, None, A, None, 8192, None) == 1           # second read missing
-    assert f(1, 2, A, None, None, A, None, 8192, None) == 1           # second write missing
-    assert f(1, 1, MIS, None, None, A, None, 8192, None) == 1         # misaligned
+    assert f(0, 1, 0, A, None, None, A, None, 8192, None) == 1        # no read stream
+    assert f(4, 1, 0, A, A, A, A, None, 8192, None) == 1               # more than 3 reads
+    assert f(1, 3, 0, A, None, None, A, A, 8192, None) == 1            # more than 2 writes
+    assert f(1, 1, 2, A, None, None, A, None, 8192, None) == 1         # no such access kind
+    assert f(1, 1, 1, A, None, None, A, None, 8191, None) == 1         # not whole 8 KB blocks
+    assert f(1, 1, 0, A, None, None, A, None, 0, None) == 1
+    assert f(2, 1, 0, A, None, None, A, None, 8192, None) == 1         # second read missing
+    assert f(1, 2, 1, A, None, None, A, None, 8192, None) == 1         # second write missing
+    assert f(1, 1, 0, MIS, None, None, A, None, 8192, None) == 1       # misaligned
 
 
 HIDDEN_ENV = {"HIP_VISIBLE_DEVICES": "-1", "ROCR_VISIBLE_DEVICES": "-1", "CUDA_VISIBLE_DEVICES": "-1"}
